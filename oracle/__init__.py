@@ -1,0 +1,197 @@
+"""fp64 CPU oracle for paged-attention decode (ctypes wrapper over pa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg. The GPU product path never imports it.
+
+The C source states the definition it computes (ROCm/aiter PR #7092, section
+"Root cause"; ROCm/aiter PR #7056, section "Summary") and the readings it takes
+where the pages leave a step open. Everything here is marshalling: numpy/torch
+CPU arrays in, fp64 numpy arrays out.
+
+Parity pins (tests/test_oracle_*.py, all CPU): brute-force dense attention on
+tiny inputs, softmax normalisation, context_len = 1, all-equal and dominant
+keys, split/merge (log-sum-exp) invariance, page-permutation invariance, GQA
+grouping, and the format decoders against torch's own casts.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+KV_DTYPES = {"bf16": 0, "fp8": 1, "mxfp4": 2}
+SCALE_MODES = {"none": 0, "tensor": 1, "token": 2}
+V_LAYOUTS = {"plain": 0, "trans": 1}
+Q_DTYPES = {"bf16": 0, "fp8": 1}
+
+
+class OracleProblem(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("qlen", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("q_per_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("scale_mode", ctypes.c_int32),
+        ("v_layout", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_double),
+    ]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (plain C, -O2, OpenMP)."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.oracle_pa_decode.restype = ctypes.c_int
+        L.oracle_pa_decode.argtypes = [ctypes.POINTER(OracleProblem), vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                       vp, vp, i32]
+        L.oracle_lse_merge.restype = None
+        L.oracle_lse_merge.argtypes = [i32, i32, vp, vp, vp, vp]
+        L.oracle_bf16_to_f64.restype = ctypes.c_double
+        L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_e4m3_to_f64.restype = ctypes.c_double
+        L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_to_f64.restype = ctypes.c_double
+        L.oracle_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_to_f64.restype = ctypes.c_double
+        L.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_e4m3_rne_sat.restype = ctypes.c_uint8
+        L.oracle_f64_to_e4m3_rne_sat.argtypes = [ctypes.c_double]
+        L.oracle_q_row_exponent.restype = ctypes.c_int
+        L.oracle_q_row_exponent.argtypes = [ctypes.c_double]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _np(x):
+    """Host numpy view of a CPU torch tensor or numpy array (bf16 viewed as uint16)."""
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        return np.ascontiguousarray(x)
+    import torch  # local: the oracle itself does not need torch
+
+    t = x.detach()
+    if t.device.type != "cpu":
+        raise ValueError("oracle inputs must be host (CPU) arrays")
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    elif t.dtype in (torch.float8_e4m3fn,):
+        t = t.view(torch.uint8)
+    return t.numpy()
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def pa_decode(case, seqs=None, t_begin=0, t_end=-1, nthreads=0, with_lse=False):
+    """fp64 attention of `case` (a paged_attention_decode_token_amd.inputs.Case or
+    any object with the same fields). Returns out [B, qlen, Hq, D] fp64 (rows of
+    sequences outside `seqs` are NaN), and lse [B, qlen, Hq] when with_lse."""
+    p = OracleProblem(
+        num_seqs=case.num_seqs, qlen=case.qlen, num_kv_heads=case.num_kv_heads, q_per_kv=case.q_per_kv,
+        head_dim=case.head_dim, page_size=case.page_size, num_blocks=case.num_blocks,
+        max_blocks_per_seq=case.max_blocks_per_seq, kv_dtype=KV_DTYPES[case.kv_dtype],
+        scale_mode=SCALE_MODES[case.scale_mode], v_layout=V_LAYOUTS[case.v_layout], q_dtype=Q_DTYPES[case.q_dtype],
+        softmax_scale=float(case.softmax_scale or 0.0))
+    arrs = [_np(case.query), _np(case.key_cache), _np(case.value_cache), _np(case.k_scale), _np(case.v_scale),
+            _np(case.block_tables).astype(np.int32), _np(case.context_lens).astype(np.int32)]
+    Hq = case.num_kv_heads * case.q_per_kv
+    out = np.full((case.num_seqs, case.qlen, Hq, case.head_dim), np.nan, dtype=np.float64)
+    lse = np.full((case.num_seqs, case.qlen, Hq), np.nan, dtype=np.float64) if with_lse else None
+    sel = None if seqs is None else np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+    rc = lib().oracle_pa_decode(ctypes.byref(p), *[_ptr(a) for a in arrs], _ptr(sel),
+                                0 if sel is None else int(sel.size), int(t_begin), int(t_end), _ptr(out), _ptr(lse),
+                                int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem description (rc=%d)" % rc)
+    return (out, lse) if with_lse else out
+
+
+def lse_merge(o_parts, lse_parts):
+    """fp64 log-sum-exp merge of per-range results: o_parts [P, D], lse_parts [P]."""
+    o = np.ascontiguousarray(np.asarray(o_parts, dtype=np.float64))
+    s = np.ascontiguousarray(np.asarray(lse_parts, dtype=np.float64))
+    out = np.zeros(o.shape[1], dtype=np.float64)
+    lse_out = np.zeros(1, dtype=np.float64)
+    lib().oracle_lse_merge(int(o.shape[0]), int(o.shape[1]), _ptr(o), _ptr(s), _ptr(out), _ptr(lse_out))
+    return out, float(lse_out[0])
+
+
+def bf16_to_f64(code):
+    return lib().oracle_bf16_to_f64(int(code) & 0xFFFF)
+
+
+def e4m3_to_f64(code):
+    return lib().oracle_e4m3_to_f64(int(code) & 0xFF)
+
+
+def e2m1_to_f64(code):
+    return lib().oracle_e2m1_to_f64(int(code) & 0xF)
+
+
+def e8m0_to_f64(code):
+    return lib().oracle_e8m0_to_f64(int(code) & 0xFF)
+
+
+def f64_to_bf16(x):
+    return lib().oracle_f64_to_bf16_rne(float(x))
+
+
+def f64_to_e4m3(x):
+    return lib().oracle_f64_to_e4m3_rne_sat(float(x))
+
+
+def q_row_exponent(amax):
+    return lib().oracle_q_row_exponent(float(amax))
+
+
+def bf16_round_array(x):
+    """Round an fp64 array to bf16 codes (uint16) with the oracle's encoder."""
+    f = lib().oracle_f64_to_bf16_rne
+    flat = np.asarray(x, dtype=np.float64).ravel()
+    return np.array([f(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(x))
+
+
+def num_threads():
+    return lib().oracle_num_threads()
+
+
+if __name__ == "__main__":  # pragma: no cover
+    build()
+    print(_LIB_PATH, file=sys.stderr)

@@ -1,0 +1,365 @@
+/*
+ * Paged-attention decode oracle: plain, slow, fp64 CPU reference.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library. The GPU product path never
+ * links, loads or calls it, and it shares no code, header, table or constant
+ * with the GPU path.
+ *
+ * What it computes (ROCm/aiter PR #7092 "pa_decode: zero V rows past the
+ * context before PV", section "Root cause"; ROCm/aiter PR #7056 "pa_decode:
+ * MXFP4 K/V in the shared PA tile kernel", section "Summary"):
+ *
+ *   for every sequence b, query token i < qlen and query head h:
+ *     kvh   = h / q_per_kv                      (heads grouped contiguously)
+ *     for t < L_b:  page = block_tables[b][t / page_size], slot = t % page_size
+ *                   s_t  = softmax_scale * dot(qhat, deq_K(page, kvh, slot))
+ *     pi_t  = exp(s_t - max s) / sum_u exp(s_u - max s)
+ *     o[d]  = sum_t pi_t * deq_V(page, kvh, slot)[d]
+ *   L_b = 0 gives o = 0.
+ *
+ * Tokens t >= L_b and block-table columns >= ceil(L_b / page_size) are never
+ * read, so whatever bytes sit in rows no sequence owns cannot reach o.
+ * All arithmetic is fp64. Each format decoder below is written from the
+ * format's own definition (OCP 8-bit floating point e4m3fn; OCP Microscaling
+ * e2m1 elements with e8m0 block scales, one per 32 elements along head_dim;
+ * bfloat16 as the top half of an IEEE binary32).
+ *
+ * Readings where the pages leave a step open are listed in the design notes
+ * of the repository; the ones that change arithmetic here are:
+ *   - softmax_scale defaults to 1/sqrt(head_dim) when the caller passes 0;
+ *   - for an MXFP4 cache with a bf16 query, every (b, i, h) query row is
+ *     quantized to e4m3 with a power-of-two scale 2^e, e the smallest integer
+ *     with max|q| <= 448 * 2^e (e = 0 for an all-zero row), round to nearest
+ *     even with saturation to +-448, and the logits are multiplied by 2^e;
+ *   - an e4m3 query is used as stored, with unit scale;
+ *   - with qlen > 1 every query row attends to all of [0, L_b) (no causal mask).
+ *
+ * Parity pins live in the test suite: brute-force dense attention, softmax
+ * normalisation, context_len = 1, split/merge invariance, page-permutation
+ * invariance and decoder tables checked against library casts.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- problem description (the oracle's own; not shared with the GPU path) ---- */
+typedef struct {
+    int32_t num_seqs, qlen, num_kv_heads, q_per_kv, head_dim, page_size;
+    int32_t num_blocks, max_blocks_per_seq;
+    int32_t kv_dtype;   /* 0 bf16, 1 fp8 e4m3fn, 2 mxfp4 (e2m1 + e8m0 per 32) */
+    int32_t scale_mode; /* 0 none, 1 per-tensor fp32[1], 2 per-token fp32 [blocks][kvh][page] */
+    int32_t v_layout;   /* 0 plain [blocks][kvh][page][D], 1 transposed [blocks][kvh][D][page] */
+    int32_t q_dtype;    /* 0 bf16, 1 e4m3fn */
+    double softmax_scale;
+} oracle_problem;
+
+enum { OR_OK = 0, OR_EINVAL = 1 };
+
+/* ---------------------------------------------------------------- decoders */
+
+/* bfloat16: the upper 16 bits of an IEEE-754 binary32. */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;
+ * S.1111.111 is NaN; exponent field 0 encodes subnormals m * 2^-9. */
+double oracle_e4m3_to_f64(uint8_t b)
+{
+    int sign = (b >> 7) & 1;
+    int e = (b >> 3) & 0xF;
+    int m = b & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* OCP MX e2m1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; all 16 codes finite.
+ * exponent field 0: subnormal 0.5 * m. */
+double oracle_e2m1_to_f64(uint8_t nibble)
+{
+    int sign = (nibble >> 3) & 1;
+    int e = (nibble >> 1) & 0x3;
+    int m = nibble & 0x1;
+    double v = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, e - 1);
+    return sign ? -v : v;
+}
+
+/* OCP MX e8m0 scale: 2^(byte - 127); byte 255 is NaN. */
+double oracle_e8m0_to_f64(uint8_t b)
+{
+    if (b == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* ----------------------------------------------------------------- encoders */
+
+/* Round an fp64 value to bfloat16, round-to-nearest-even (NaN -> 0x7FC0).
+ * Obvious form: binary-search the two non-negative codes whose values bracket
+ * |x| (codes are monotone in value), take the nearer, ties to the even code.
+ * Above the largest finite value the upper neighbour is infinity, which counts
+ * as 2^128 for the distance, as IEEE-754 rounding does. */
+uint16_t oracle_f64_to_bf16_rne(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double ax = fabs(x);
+    if (isinf(ax))
+        return (uint16_t)(sign | 0x7F80);
+    uint16_t lo = 0, hi = 0x7F80;
+    while (hi - lo > 1) {
+        uint16_t mid = (uint16_t)((lo + hi) / 2);
+        if (oracle_bf16_to_f64(mid) <= ax)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double vlo = oracle_bf16_to_f64(lo);
+    double vhi = (hi == 0x7F80) ? ldexp(1.0, 128) : oracle_bf16_to_f64(hi);
+    double dlo = ax - vlo, dhi = vhi - ax;
+    uint16_t pick;
+    if (dlo < dhi)
+        pick = lo;
+    else if (dhi < dlo)
+        pick = hi;
+    else
+        pick = (lo & 1) ? hi : lo;
+    return (uint16_t)(sign | pick);
+}
+
+/* Round an fp64 value to OCP e4m3fn, nearest with ties to the even code,
+ * saturating to +-448 (no NaN output for finite input). Brute force over the
+ * 127 non-negative finite codes. */
+uint8_t oracle_f64_to_e4m3_rne_sat(double x)
+{
+    uint8_t sign = (x < 0) ? 0x80 : 0;
+    double ax = fabs(x);
+    int best = 0;
+    double bestd = INFINITY;
+    if (isnan(x))
+        return 0x7F;
+    if (ax >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    for (int c = 0; c <= 0x7E; c++) {
+        double d = fabs(oracle_e4m3_to_f64((uint8_t)c) - ax);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            bestd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Power-of-two exponent for one query row: the smallest e with amax <= 448 * 2^e
+ * (0 for an all-zero row). */
+int oracle_q_row_exponent(double amax)
+{
+    if (!(amax > 0.0))
+        return 0;
+    int e = -160;
+    while (amax > ldexp(448.0, e))
+        e++;
+    return e;
+}
+
+/* ------------------------------------------------------------- cache reads */
+
+static double kv_elem(const oracle_problem* p, const void* cache, const void* scale_mx, int64_t page, int kvh,
+                      int slot, int d, int transposed)
+{
+    const int64_t PG = p->page_size, D = p->head_dim, H = p->num_kv_heads;
+    if (p->kv_dtype == 2) {
+        const uint8_t* data = (const uint8_t*)cache;
+        const uint8_t* sc = (const uint8_t*)scale_mx;
+        int64_t row = (page * H + kvh) * PG + slot;
+        uint8_t byte = data[row * (D / 2) + d / 2];
+        uint8_t nib = (d % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+        return oracle_e2m1_to_f64(nib) * oracle_e8m0_to_f64(sc[row * (D / 32) + d / 32]);
+    }
+    int64_t idx;
+    if (transposed)
+        idx = ((page * H + kvh) * D + d) * PG + slot;
+    else
+        idx = ((page * H + kvh) * PG + slot) * D + d;
+    if (p->kv_dtype == 0)
+        return oracle_bf16_to_f64(((const uint16_t*)cache)[idx]);
+    return oracle_e4m3_to_f64(((const uint8_t*)cache)[idx]);
+}
+
+static double token_scale(const oracle_problem* p, const void* scale, int64_t page, int kvh, int slot)
+{
+    if (p->kv_dtype == 2 || p->scale_mode == 0)
+        return 1.0;
+    const float* s = (const float*)scale;
+    if (p->scale_mode == 1)
+        return (double)s[0];
+    return (double)s[(page * p->num_kv_heads + kvh) * p->page_size + slot];
+}
+
+/* ------------------------------------------------------------------ decode */
+
+/*
+ * oracle_pa_decode: attention of every selected sequence over its tokens
+ * [t_begin, min(t_end, L_b)). With t_begin = 0 and t_end < 0 the range is the
+ * whole context. out: fp64 [num_seqs][qlen][Hq][D], normalised over the range
+ * (0 for an empty range). lse (nullable): fp64 [num_seqs][qlen][Hq], the
+ * natural log of sum_t exp(s_t) over the range (-inf for an empty range).
+ * seqs (nullable): the sequence indices to compute; rows of other sequences
+ * are left untouched. Returns 0, or 1 for an invalid description.
+ */
+int oracle_pa_decode(const oracle_problem* p, const void* query, const void* key_cache, const void* value_cache,
+                     const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* seqs, int32_t n_seqs, int32_t t_begin,
+                     int32_t t_end, double* out, double* lse, int32_t nthreads)
+{
+    if (!p || p->num_seqs < 0 || p->qlen < 1 || p->num_kv_heads < 1 || p->q_per_kv < 1 || p->head_dim < 1 ||
+        p->page_size < 1 || p->max_blocks_per_seq < 0 || p->num_blocks < 1)
+        return OR_EINVAL;
+    if (p->kv_dtype == 2 && (p->head_dim % 32) != 0)
+        return OR_EINVAL;
+    const int B = p->num_seqs, QL = p->qlen, H = p->num_kv_heads, G = p->q_per_kv, D = p->head_dim;
+    const int Hq = H * G;
+    const double sigma = (p->softmax_scale != 0.0) ? p->softmax_scale : 1.0 / sqrt((double)D);
+    const int nsel = seqs ? n_seqs : B;
+    const int transposed = (p->v_layout == 1);
+    const void* k_mx = (p->kv_dtype == 2) ? k_scale : NULL;
+    const void* v_mx = (p->kv_dtype == 2) ? v_scale : NULL;
+    int npairs = nsel * H;
+
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int pair = 0; pair < npairs; pair++) {
+        int b = seqs ? seqs[pair / H] : pair / H;
+        int kvh = pair % H;
+        int L = context_lens[b];
+        int t0 = t_begin < 0 ? 0 : t_begin;
+        int t1 = (t_end < 0 || t_end > L) ? L : t_end;
+        int n = t1 > t0 ? t1 - t0 : 0;
+        double* qhat = (double*)malloc(sizeof(double) * (size_t)D);
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+        for (int i = 0; i < QL; i++) {
+            for (int hg = 0; hg < G; hg++) {
+                int h = kvh * G + hg;
+                int64_t row = ((int64_t)b * QL + i) * Hq + h;
+                double* o = out + row * D;
+                /* query row */
+                double qscale = 1.0;
+                if (p->q_dtype == 1) {
+                    const uint8_t* q8 = (const uint8_t*)query + row * D;
+                    for (int d = 0; d < D; d++)
+                        qhat[d] = oracle_e4m3_to_f64(q8[d]);
+                } else {
+                    const uint16_t* q16 = (const uint16_t*)query + row * D;
+                    for (int d = 0; d < D; d++)
+                        qhat[d] = oracle_bf16_to_f64(q16[d]);
+                    if (p->kv_dtype == 2) {
+                        double amax = 0.0;
+                        for (int d = 0; d < D; d++)
+                            if (fabs(qhat[d]) > amax)
+                                amax = fabs(qhat[d]);
+                        int e = oracle_q_row_exponent(amax);
+                        for (int d = 0; d < D; d++)
+                            qhat[d] = oracle_e4m3_to_f64(oracle_f64_to_e4m3_rne_sat(ldexp(qhat[d], -e)));
+                        qscale = ldexp(1.0, e);
+                    }
+                }
+                /* scores */
+                double mx = -INFINITY;
+                for (int j = 0; j < n; j++) {
+                    int t = t0 + j;
+                    int64_t page = block_tables[(int64_t)b * p->max_blocks_per_seq + t / p->page_size];
+                    int slot = t % p->page_size;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; d++)
+                        dot += qhat[d] * kv_elem(p, key_cache, k_mx, page, kvh, slot, d, 0);
+                    s[j] = sigma * qscale * token_scale(p, k_scale, page, kvh, slot) * dot;
+                    if (s[j] > mx)
+                        mx = s[j];
+                }
+                /* softmax and weighted sum of V rows */
+                double den = 0.0;
+                for (int d = 0; d < D; d++)
+                    acc[d] = 0.0;
+                for (int j = 0; j < n; j++) {
+                    int t = t0 + j;
+                    int64_t page = block_tables[(int64_t)b * p->max_blocks_per_seq + t / p->page_size];
+                    int slot = t % p->page_size;
+                    double w = exp(s[j] - mx);
+                    double vs = token_scale(p, v_scale, page, kvh, slot);
+                    den += w;
+                    for (int d = 0; d < D; d++)
+                        acc[d] += w * vs * kv_elem(p, value_cache, v_mx, page, kvh, slot, d, transposed);
+                }
+                for (int d = 0; d < D; d++)
+                    o[d] = (n > 0) ? acc[d] / den : 0.0;
+                if (lse)
+                    lse[row] = (n > 0) ? mx + log(den) : -INFINITY;
+            }
+        }
+        free(qhat);
+        free(s);
+        free(acc);
+    }
+    return OR_OK;
+}
+
+/*
+ * oracle_lse_merge: combine attention results over disjoint token ranges.
+ * o_parts: [nparts][D] each normalised over its range, lse_parts: [nparts].
+ * Result: sum_p exp(lse_p - LSE) o_p with LSE = log sum_p exp(lse_p); parts
+ * with lse = -inf contribute nothing; all-empty gives 0.
+ */
+void oracle_lse_merge(int32_t nparts, int32_t D, const double* o_parts, const double* lse_parts, double* out,
+                      double* lse_out)
+{
+    double mx = -INFINITY;
+    for (int p = 0; p < nparts; p++)
+        if (lse_parts[p] > mx)
+            mx = lse_parts[p];
+    for (int d = 0; d < D; d++)
+        out[d] = 0.0;
+    if (mx == -INFINITY) {
+        if (lse_out)
+            *lse_out = -INFINITY;
+        return;
+    }
+    double den = 0.0;
+    for (int p = 0; p < nparts; p++)
+        den += exp(lse_parts[p] - mx);
+    for (int p = 0; p < nparts; p++) {
+        double w = exp(lse_parts[p] - mx) / den;
+        for (int d = 0; d < D; d++)
+            out[d] += w * o_parts[(int64_t)p * D + d];
+    }
+    if (lse_out)
+        *lse_out = mx + log(den);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

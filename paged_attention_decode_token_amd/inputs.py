@@ -1,0 +1,343 @@
+"""Seeded synthetic inputs for paged-attention decode.
+
+This module only draws random numbers and lays them out in the cache formats;
+it holds none of the attention arithmetic. The GPU path (through the C ABI)
+and the fp64 oracle both read what it builds.
+
+Layouts (the same ones the C ABI documents):
+  query          [num_seqs, qlen, Hq, D]        bf16, or e4m3fn bytes (MXFP4 only)
+  key/value      [num_blocks, Hkv, page, D]     bf16 or e4m3fn bytes
+  value, trans   [num_blocks, Hkv, D, page]     (transposed V)
+  MXFP4 data     [num_blocks, Hkv, page, D/2]   uint8, element 2i in the low nibble
+  MXFP4 scales   [num_blocks, Hkv, page, D/32]  uint8 e8m0 (passed as k_scale / v_scale)
+  per-tensor     fp32 [1] each for K and V
+  per-token      fp32 [num_blocks, Hkv, page] each for K and V
+  block_tables   [num_seqs, max_blocks_per_seq] int32
+  context_lens   [num_seqs] int32
+
+Structure (ROCm/aiter PR #7092, section "Tests"): each sequence's pages are the
+next ceil(L/page) entries of a seeded permutation of pages 1..N, so block 0 is
+never owned; every table row ends with at least 2 padded columns that point to
+block 0. Rows no sequence owns -- all of block 0 and the tail of each last page
+past the context length -- receive the requested fill ("zero", "nan", "inf" or
+"random"), together with their per-token or block scales.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import torch
+
+PAGE_TILE = 256  # tokens per planning tile (PR #7092, "Root cause")
+
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    name: str
+    num_seqs: int
+    lens: tuple  # ("fixed", (l0, l1, ...)) | ("uniform", lo, hi) | ("const", L)
+    qlen: int
+    num_kv_heads: int
+    q_per_kv: int
+    head_dim: int
+    page_size: int
+    kv_dtype: str  # bf16 | fp8 | mxfp4
+    scale_mode: str = "none"  # none | tensor | token
+    v_layout: str = "plain"  # plain | trans
+    q_dtype: str = "bf16"  # bf16 | fp8
+    fill: str = "nan"  # nan | inf | zero | random
+    seed: int = 0
+    pad_cols: int = 2
+
+    def replace(self, **kw) -> "Spec":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclasses.dataclass
+class Case:
+    spec: Spec
+    num_seqs: int
+    qlen: int
+    num_kv_heads: int
+    q_per_kv: int
+    head_dim: int
+    page_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    max_context_len: int
+    kv_dtype: str
+    scale_mode: str
+    v_layout: str
+    q_dtype: str
+    softmax_scale: float
+    query: torch.Tensor
+    key_cache: torch.Tensor
+    value_cache: torch.Tensor
+    k_scale: Optional[torch.Tensor]
+    v_scale: Optional[torch.Tensor]
+    block_tables: torch.Tensor
+    context_lens: torch.Tensor
+
+    @property
+    def num_q_heads(self) -> int:
+        return self.num_kv_heads * self.q_per_kv
+
+    def kv_bytes_per_token_head(self) -> int:
+        D = self.head_dim
+        if self.kv_dtype == "bf16":
+            return 4 * D
+        if self.kv_dtype == "fp8":
+            return 2 * D + (8 if self.scale_mode == "token" else 0)
+        return 2 * (D // 2 + D // 32)
+
+    def kv_bytes(self, seqs: Optional[Sequence[int]] = None) -> int:
+        """Bytes of K, V and their scales for the owned tokens (nominal KV payload)."""
+        lens = self.context_lens.tolist()
+        if seqs is not None:
+            lens = [lens[i] for i in seqs]
+        return sum(lens) * self.num_kv_heads * self.kv_bytes_per_token_head()
+
+    def tensors(self):
+        return dict(query=self.query, key_cache=self.key_cache, value_cache=self.value_cache,
+                    k_scale=self.k_scale, v_scale=self.v_scale, block_tables=self.block_tables,
+                    context_lens=self.context_lens)
+
+
+# ---------------------------------------------------------------- workloads
+
+def _spec(name, **kw):
+    return Spec(name=name, **kw)
+
+
+# Workloads at their stated sizes.
+TINY_BF16 = _spec("tiny_bf16_p16", num_seqs=4, lens=("fixed", (1, 17, 255, 257)), qlen=1, num_kv_heads=1,
+                  q_per_kv=8, head_dim=128, page_size=16, kv_dtype="bf16", fill="nan", seed=1000)
+BF16_P64 = _spec("bf16_p64_b64", num_seqs=64, lens=("uniform", 1000, 8192), qlen=1, num_kv_heads=8, q_per_kv=8,
+                 head_dim=128, page_size=64, kv_dtype="bf16", fill="inf", seed=1001)
+BF16_P128 = BF16_P64.replace(name="bf16_p128_b64", page_size=128, seed=1002)
+FP8TOK_Q1 = _spec("fp8tok_p16_b16_q1", num_seqs=16, lens=("uniform", 2048, 32768), qlen=1, num_kv_heads=2,
+                  q_per_kv=8, head_dim=256, page_size=16, kv_dtype="fp8", scale_mode="token", fill="nan", seed=1003)
+FP8TOK_Q4 = FP8TOK_Q1.replace(name="fp8tok_p16_b16_q4", qlen=4, seed=1004)
+FP8_TRANS = _spec("fp8_transv_p128_b256", num_seqs=256, lens=("const", 16384), qlen=1, num_kv_heads=1, q_per_kv=16,
+                  head_dim=128, page_size=128, kv_dtype="fp8", scale_mode="tensor", v_layout="trans", fill="nan",
+                  seed=1005)
+MXFP4_SHORT_Q8 = _spec("mxfp4_p128_b16_l2048_qfp8", num_seqs=16, lens=("const", 2048), qlen=1, num_kv_heads=4,
+                       q_per_kv=16, head_dim=128, page_size=128, kv_dtype="mxfp4", q_dtype="fp8", fill="nan",
+                       seed=1006)
+MXFP4_SHORT_QBF = MXFP4_SHORT_Q8.replace(name="mxfp4_p128_b16_l2048_qbf16", q_dtype="bf16", seed=1007)
+MXFP4_LONG_Q8 = MXFP4_SHORT_Q8.replace(name="mxfp4_p128_b16_l131072_qfp8", lens=("const", 131072), seed=1008)
+MXFP4_LONG_QBF = MXFP4_LONG_Q8.replace(name="mxfp4_p128_b16_l131072_qbf16", q_dtype="bf16", seed=1009)
+
+FULL = [TINY_BF16, BF16_P64, BF16_P128, FP8TOK_Q1, FP8TOK_Q4, FP8_TRANS, MXFP4_SHORT_Q8, MXFP4_SHORT_QBF,
+        MXFP4_LONG_Q8, MXFP4_LONG_QBF]
+BY_NAME = {s.name: s for s in FULL}
+
+
+def small(spec: Spec) -> Spec:
+    """Same structure at sizes the oracle finishes in about a second: several
+    256-token tiles, ragged tails, all head/page/dtype parameters unchanged."""
+    kind = spec.lens[0]
+    if kind == "fixed":
+        return spec
+    if spec.name.startswith("bf16"):
+        return spec.replace(name=spec.name + "_small", num_seqs=5, num_kv_heads=2, lens=("uniform", 1, 1500))
+    if spec.name.startswith("fp8tok"):
+        return spec.replace(name=spec.name + "_small", num_seqs=4, lens=("uniform", 200, 1400))
+    if spec.name.startswith("fp8_trans"):
+        return spec.replace(name=spec.name + "_small", num_seqs=4, lens=("fixed", (1024, 1024, 768, 1280)))
+    if spec.name.startswith("mxfp4"):
+        return spec.replace(name=spec.name + "_small", num_seqs=3, num_kv_heads=2, lens=("fixed", (1, 300, 1100)))
+    return spec
+
+
+# ---------------------------------------------------------------- generation
+
+def _lens(spec: Spec, g: torch.Generator):
+    kind = spec.lens[0]
+    if kind == "fixed":
+        vals = list(spec.lens[1])
+        assert len(vals) == spec.num_seqs
+        return vals
+    if kind == "const":
+        return [int(spec.lens[1])] * spec.num_seqs
+    lo, hi = spec.lens[1], spec.lens[2]
+    return torch.randint(lo, hi + 1, (spec.num_seqs,), generator=g).tolist()
+
+
+def _randn(shape, g, chunk=1 << 26):
+    """float32 N(0,1) drawn in chunks (keeps peak memory bounded)."""
+    n = math.prod(shape)
+    out = torch.empty(n, dtype=torch.float32)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = torch.randn(e - s, generator=g)
+    return out.view(*shape)
+
+
+def _randn_to(shape, g, dtype, scale=None, chunk=1 << 26):
+    """N(0,1) cast to `dtype` chunk by chunk (values divided by `scale` first and
+    clamped to the e4m3 range when dtype is float8)."""
+    n = math.prod(shape)
+    out = torch.empty(n, dtype=dtype)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = torch.randn(e - s, generator=g)
+        if scale is not None:
+            x = x / scale
+        if dtype == torch.float8_e4m3fn:
+            x = x.clamp_(-448.0, 448.0)
+        out[s:e] = x.to(dtype)
+    return out.view(*shape)
+
+
+def _poison_value(kind, fill, g, n):
+    """Fill pattern for n unowned elements of a given storage kind."""
+    if fill == "zero":
+        base = {"bf16": torch.zeros(n, dtype=torch.int16), "u8": torch.zeros(n, dtype=torch.uint8),
+                "f32": torch.zeros(n, dtype=torch.float32), "e8m0": torch.zeros(n, dtype=torch.uint8)}
+        return base[kind]
+    if fill == "random":
+        if kind == "bf16":
+            return torch.randint(-32768, 32768, (n,), generator=g, dtype=torch.int32).to(torch.int16)
+        if kind in ("u8", "e8m0"):
+            return torch.randint(0, 256, (n,), generator=g, dtype=torch.int32).to(torch.uint8)
+        return torch.randint(-2 ** 31, 2 ** 31, (n,), generator=g, dtype=torch.int64).to(torch.int32).view(
+            torch.float32)
+    if fill == "nan":
+        return {"bf16": torch.full((n,), 0x7FC0, dtype=torch.int16),
+                "u8": torch.full((n,), 0xFF, dtype=torch.uint8),
+                "f32": torch.full((n,), float("nan")),
+                "e8m0": torch.full((n,), 0xFF, dtype=torch.uint8)}[kind]
+    if fill == "inf":
+        alt = torch.arange(n) % 2 == 0
+        if kind == "bf16":
+            return torch.where(alt, torch.tensor(0x7F80, dtype=torch.int16),
+                               torch.tensor(-128, dtype=torch.int16))  # 0x7F80 / 0xFF80
+        if kind == "u8":  # e4m3 has no infinity: +-448 (0x7E / 0xFE)
+            return torch.where(alt, torch.tensor(0x7E, dtype=torch.uint8), torch.tensor(0xFE, dtype=torch.uint8))
+        if kind == "e8m0":  # largest finite scale, 2^127
+            return torch.full((n,), 0xFE, dtype=torch.uint8)
+        return torch.where(alt, torch.tensor(float("inf")), torch.tensor(float("-inf")))
+    raise ValueError(fill)
+
+
+def make_case(spec: Spec, fill: Optional[str] = None, seed: Optional[int] = None) -> Case:
+    """Build one seeded case on the host. The owned content depends only on
+    (spec, seed); `fill` changes only the rows no sequence owns."""
+    fill = spec.fill if fill is None else fill
+    seed = spec.seed if seed is None else seed
+    g = torch.Generator().manual_seed(seed)
+    B, QL, H, G, D, PG = spec.num_seqs, spec.qlen, spec.num_kv_heads, spec.q_per_kv, spec.head_dim, spec.page_size
+    Hq = H * G
+    lens = _lens(spec, g)
+    npages = [(L + PG - 1) // PG for L in lens]
+    N = sum(npages)
+    num_blocks = N + 1
+    width = max(npages + [0]) + spec.pad_cols
+    perm = (torch.randperm(N, generator=g) + 1).to(torch.int32) if N > 0 else torch.zeros(0, dtype=torch.int32)
+    bt = torch.zeros(B, width, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :npages[b]] = perm[off:off + npages[b]]
+        off += npages[b]
+
+    # query
+    if spec.q_dtype == "fp8":
+        query = _randn_to((B, QL, Hq, D), g, torch.float8_e4m3fn)
+    else:
+        query = _randn_to((B, QL, Hq, D), g, torch.bfloat16)
+
+    k_scale = v_scale = None
+    if spec.kv_dtype == "bf16":
+        K = _randn_to((num_blocks, H, PG, D), g, torch.bfloat16)
+        V = _randn_to((num_blocks, H, PG, D), g, torch.bfloat16)
+    elif spec.kv_dtype == "fp8":
+        if spec.scale_mode == "tensor":
+            Kf = _randn((num_blocks, H, PG, D), g)
+            Vf = _randn((num_blocks, H, PG, D), g)
+            ks = float(Kf.abs().max()) / 448.0
+            vs = float(Vf.abs().max()) / 448.0
+            ks32 = torch.tensor([ks], dtype=torch.float32)
+            vs32 = torch.tensor([vs], dtype=torch.float32)
+            K = (Kf / ks32).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+            V = (Vf / vs32).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+            del Kf, Vf
+            k_scale, v_scale = ks32, vs32
+        else:
+            K = _randn_to((num_blocks, H, PG, D), g, torch.float8_e4m3fn)
+            V = _randn_to((num_blocks, H, PG, D), g, torch.float8_e4m3fn)
+            if spec.scale_mode == "token":
+                k_scale = torch.rand(num_blocks, H, PG, generator=g) * 0.09 + 0.01
+                v_scale = torch.rand(num_blocks, H, PG, generator=g) * 0.09 + 0.01
+        K = K.view(torch.uint8)
+        V = V.view(torch.uint8)
+    elif spec.kv_dtype == "mxfp4":
+        K = torch.randint(0, 256, (num_blocks, H, PG, D // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+        V = torch.randint(0, 256, (num_blocks, H, PG, D // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+        k_scale = torch.randint(118, 137, (num_blocks, H, PG, D // 32), generator=g, dtype=torch.int32).to(
+            torch.uint8)
+        v_scale = torch.randint(118, 137, (num_blocks, H, PG, D // 32), generator=g, dtype=torch.int32).to(
+            torch.uint8)
+    else:
+        raise ValueError(spec.kv_dtype)
+
+    # unowned (page, slot) pairs: all of block 0, then every last-page tail
+    pages = [torch.zeros(PG, dtype=torch.int64)]
+    slots = [torch.arange(PG, dtype=torch.int64)]
+    for b in range(B):
+        L = lens[b]
+        if L > 0 and L % PG != 0:
+            last = int(bt[b, npages[b] - 1])
+            s = torch.arange(L % PG, PG, dtype=torch.int64)
+            pages.append(torch.full_like(s, last))
+            slots.append(s)
+    up = torch.cat(pages)
+    us = torch.cat(slots)
+    n_un = int(up.numel())
+    gp = torch.Generator().manual_seed(seed + 7919)  # poison stream, independent of the owned content
+
+    def poison_rows(t: torch.Tensor, kind: str):
+        # t: [num_blocks, H, PG] or [num_blocks, H, PG, X], all in token-major layout
+        store = t.view(torch.int16) if kind == "bf16" else t
+        if t.dim() == 3:
+            store[up, :, us] = _poison_value(kind, fill, gp, n_un * H).view(n_un, H)
+        else:
+            X = t.shape[3]
+            store[up, :, us, :] = _poison_value(kind, fill, gp, n_un * H * X).view(n_un, H, X)
+
+    if spec.kv_dtype == "bf16":
+        poison_rows(K, "bf16")
+        poison_rows(V, "bf16")
+    elif spec.kv_dtype == "fp8":
+        poison_rows(K, "u8")
+        poison_rows(V, "u8")
+        if spec.scale_mode == "token":
+            poison_rows(k_scale, "f32")
+            poison_rows(v_scale, "f32")
+    else:
+        poison_rows(K, "u8")
+        poison_rows(V, "u8")
+        poison_rows(k_scale, "e8m0")
+        poison_rows(v_scale, "e8m0")
+    if spec.v_layout == "trans":
+        V = V.transpose(2, 3).contiguous()  # [num_blocks, H, D, PG]
+
+    return Case(spec=spec, num_seqs=B, qlen=QL, num_kv_heads=H, q_per_kv=G, head_dim=D, page_size=PG,
+                num_blocks=num_blocks, max_blocks_per_seq=width, max_context_len=max(lens + [0]),
+                kv_dtype=spec.kv_dtype, scale_mode=spec.scale_mode, v_layout=spec.v_layout, q_dtype=spec.q_dtype,
+                softmax_scale=0.0, query=query, key_cache=K, value_cache=V, k_scale=k_scale, v_scale=v_scale,
+                block_tables=bt, context_lens=torch.tensor(lens, dtype=torch.int32))
+
+
+def owned_mask(case: Case) -> torch.Tensor:
+    """Boolean [num_blocks, page] map of the (page, slot) rows some sequence owns."""
+    m = torch.zeros(case.num_blocks, case.page_size, dtype=torch.bool)
+    PG = case.page_size
+    for b in range(case.num_seqs):
+        L = int(case.context_lens[b])
+        for j in range((L + PG - 1) // PG):
+            p = int(case.block_tables[b, j])
+            m[p, :min(PG, L - j * PG)] = True
+    return m
