@@ -1,0 +1,184 @@
+"""Benchmark of the paged-attention decode hot path on one MI355X.
+
+One step = one pa_decode call over each page-size variant of the bf16
+workload (batch 64, context lengths uniform in [1000, 8192], 8 KV heads x 8
+query heads each, head_dim 128, qlen 1, pages of 64 and of 128 tokens), with
+every input resident in HBM. The metric is the nominal KV payload (K and V
+bytes of the owned tokens) per second.
+
+Prints one JSON line. Besides the contract keys it carries:
+  roofline      the tile kernel's achieved GB/s (algorithmic bytes per launch /
+                average launch duration from HIP events recorded around each
+                launch on the launch stream) against the 8 TB/s HBM peak, and
+                the HBM traffic from rocprofv3 counters when a counter summary
+                of the current kernel source is committed under profiles/;
+  cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample of
+                the same workload (the oracle is test infrastructure and is
+                used here only for that baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV-read HBM GB/s and % of peak; µs per pa_decode call per config"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("pa_kernels.hip", "pa_internal.h"):
+        with open(os.path.join(ROOT, "paged_attention_decode_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_tag: str):
+    """HBM bytes per launch from a committed counter summary of this kernel source, else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source") != kernel_source_hash():
+        return None
+    ent = d.get("kernels", {}).get(kernel_tag)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def time_cpu_oracle(case, target_s=15.0):
+    import oracle
+
+    # one sequence first, then as many more as fit the time budget
+    t0 = time.perf_counter()
+    oracle.pa_decode(case, seqs=[0])
+    dt = time.perf_counter() - t0
+    n = max(1, min(case.num_seqs, int(target_s / max(dt, 1e-3))))
+    seqs = list(range(n))
+    t0 = time.perf_counter()
+    oracle.pa_decode(case, seqs=seqs)
+    dt = time.perf_counter() - t0
+    nbytes = case.kv_bytes(seqs)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d sequences (%.0f MB of KV) of the page-64 variant, %.1f s" % (
+                n, case.num_seqs, nbytes / 1e6, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_attention_decode_token_amd as pa
+    from paged_attention_decode_token_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    pa.lib()
+
+    variants = []
+    for spec in (I.BF16_P64, I.BF16_P128):
+        case = I.make_case(spec)
+        d = pa.device_tensors(case)
+        plan = pa.pa_plan(pa.problem_of(case), case.context_lens)
+        out = torch.empty((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+        variants.append(dict(spec=spec, case=case, d=d, plan=plan, out=out, bytes=case.kv_bytes()))
+    torch.cuda.synchronize()
+
+    def step():
+        for v in variants:
+            d = v["d"]
+            pa.pa_decode(v["plan"], d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
+                         d["block_tables"], d["context_lens"], v["out"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.calibrate_copy:
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        y = torch.empty_like(x)
+        torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        del x, y
+    for v in variants:
+        v["plan"].set_timing(True, args.steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    per = {}
+    tile_bytes = tile_ms = 0.0
+    for v in variants:
+        t_ms, m_ms, n = v["plan"].read_timing()
+        v["plan"].set_timing(False)
+        tile_avg = t_ms / n
+        merge_avg = m_ms / n
+        per[v["spec"].name] = {"us_per_call": round((t_ms + m_ms) / n * 1e3, 2), "tile_us": round(tile_avg * 1e3, 2),
+                               "merge_us": round(merge_avg * 1e3, 2), "kv_bytes": v["bytes"],
+                               "kv_GBps": round(v["bytes"] / ((t_ms + m_ms) / n * 1e-3) / 1e9, 1),
+                               "tasks": v["plan"].info().num_tasks, "partitions_max": v["plan"].info().max_parts}
+        tile_bytes += v["bytes"]
+        tile_ms += tile_avg
+    step_bytes = sum(v["bytes"] for v in variants)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    achieved = tile_bytes / (tile_ms * 1e-3) / 1e9
+    traffic = None
+    tr = [load_traffic(v["spec"].name) for v in variants]
+    if all(t is not None for t in tr):
+        traffic = sum(tr)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 paged decode, page 64 and page 128 variants (one call each per step), "
+                               "batch 64, context U[1000, 8192], 8 KV heads x GQA 8, head_dim 128, qlen 1",
+                   "global_batch": 64, "seq_len": "U[1000,8192]", "parallelism": "none (1 GPU)"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "per_call": per,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "pa_tile_kernel (bf16, D 128, page 64 and 128)",
+                     "algorithmic_bytes_per_step": tile_bytes},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = time_cpu_oracle(variants[0]["case"])
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

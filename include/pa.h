@@ -1,0 +1,220 @@
+/*
+ * pa.h -- C ABI of the paged-attention decode library (libpa.so, gfx950 / MI355X).
+ *
+ * One decode step of attention over a paged KV cache: for every sequence b,
+ * query token i < qlen and query head h, read K/V through the page block
+ * table up to context_lens[b], score Q against K, softmax, multiply by V, and
+ * merge the per-partition partial results (ROCm/aiter PR #7092 "pa_decode:
+ * zero V rows past the context before PV", sections "Root cause" and "Fix";
+ * ROCm/aiter PR #7056 "pa_decode: MXFP4 K/V in the shared PA tile kernel",
+ * sections "Summary" and "Behavior and intent").
+ *
+ *   kvh       = h / q_per_kv                                (heads grouped contiguously)
+ *   s_t       = softmax_scale * dot(qhat, K_t)              for t < L = context_lens[b]
+ *   out[b,i,h]= sum_t softmax(s)_t * V_t                    (bf16, round to nearest even)
+ *   L = 0     -> out row = 0
+ *
+ * Rows no sequence owns (block 0 pinned pages, the tail of a sequence's last
+ * page, anything at or past L) never influence out: their scores are -inf,
+ * and on the boundary tile their V bytes and per-token scales are zeroed
+ * before the P*V product (PR #7092, section "Fix"). NaN/Inf there is harmless.
+ *
+ * Everything is plain C: pointers, sizes and enums. PyTorch (or any caller)
+ * owns the device tensors; the library owns only what pa_plan allocates.
+ *
+ * Error behaviour: every entry point returns a pa_status; on failure,
+ * pa_last_error() gives a thread-local message. No entry point aborts or
+ * throws across the ABI.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. PA_ERR_INVALID_ARG: malformed input (NULL, misaligned,
+ * inconsistent sizes). PA_ERR_UNSUPPORTED: well-formed but outside what the
+ * kernels implement (e.g. MXFP4 with page size 64, head_dim 64, not gfx950).
+ * PA_ERR_HIP: a HIP runtime call failed. PA_ERR_OOM: device allocation failed. */
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,
+    PA_ERR_UNSUPPORTED = 2,
+    PA_ERR_HIP = 3,
+    PA_ERR_OOM = 4
+} pa_status;
+
+/* KV cache element formats.
+ * PA_KV_BF16      : bfloat16.
+ * PA_KV_FP8_E4M3  : OCP e4m3fn bytes (bias 7, max 448, S.1111.111 = NaN), with
+ *                   per-tensor or per-token fp32 scales (PR #7092, "Tests").
+ * PA_KV_MXFP4     : OCP MX e2m1 pairs (element 2i in the low nibble) plus one
+ *                   e8m0 scale byte per 32 elements along head_dim (PR #7056,
+ *                   "Summary"). */
+typedef enum pa_kv_dtype { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1, PA_KV_MXFP4 = 2 } pa_kv_dtype;
+
+typedef enum pa_scale_mode {
+    PA_SCALE_NONE = 0,       /* bf16 and MXFP4 (MXFP4 carries its own block scales) */
+    PA_SCALE_PER_TENSOR = 1, /* fp8: k_scale, v_scale = device fp32[1] each          */
+    PA_SCALE_PER_TOKEN = 2   /* fp8: k_scale, v_scale = device fp32 [num_blocks][Hkv][page_size] */
+} pa_scale_mode;
+
+/* V layout. PLAIN: [num_blocks][Hkv][page_size][head_dim] (token-major, like K).
+ * TRANSPOSED ("trans_v", PR #7092 "Tests"): [num_blocks][Hkv][head_dim][page_size]. */
+typedef enum pa_v_layout { PA_V_PLAIN = 0, PA_V_TRANSPOSED = 1 } pa_v_layout;
+
+/* Query format. PA_Q_FP8_E4M3 is accepted only with an MXFP4 cache, where it is
+ * used as stored with unit scale (PR #7056, "Summary"). A bf16 query with an
+ * MXFP4 cache is quantized to e4m3 per (sequence, query token, head) row with
+ * a power-of-two scale 2^e, e the smallest integer with max|q| <= 448 * 2^e. */
+typedef enum pa_q_dtype { PA_Q_BF16 = 0, PA_Q_FP8_E4M3 = 1 } pa_q_dtype;
+
+/* Problem descriptor. All sizes are element counts unless stated.
+ *   num_seqs            B, sequences in the batch (>= 0)
+ *   qlen                query tokens per sequence (1..4 typical; rows = qlen * q_per_kv <= 32)
+ *   num_kv_heads        Hkv
+ *   q_per_kv            G, query heads per KV head (Hq = Hkv * G)
+ *   head_dim            D: 128 or 256 (MXFP4: 128)
+ *   page_size           tokens per page: 16, 64 or 128 (MXFP4: 128)
+ *   num_blocks          pages in the pool (>= 1; block 0 always exists)
+ *   max_blocks_per_seq  width of block_tables
+ *   max_context_len     upper bound of context_lens (used when no host lengths are given)
+ *   kv_dtype, scale_mode, v_layout, q_dtype   see the enums (MXFP4: PLAIN only)
+ *   softmax_scale       0 -> 1/sqrt(head_dim)
+ *   max_partitions      0 -> 64; upper bound of partitions per sequence
+ *   task_budget         0 -> 2 * compute units; target number of workgroups
+ *   mxfp4_scaled_qk     MXFP4 only. 0 (default): K is widened exactly to bf16 and
+ *                       QK runs on the bf16 MFMA. 1: QK runs on the block-scaled
+ *                       fp4 x fp8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) with
+ *                       the query in e4m3 -- faster, but on gfx950 that
+ *                       instruction sums some operand mixes to only about 2^-13
+ *                       of their largest product, so near-tied logits can move
+ *                       single output elements beyond 2e-2.
+ */
+typedef struct pa_problem {
+    int32_t num_seqs;
+    int32_t qlen;
+    int32_t num_kv_heads;
+    int32_t q_per_kv;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_blocks;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    int32_t kv_dtype;
+    int32_t scale_mode;
+    int32_t v_layout;
+    int32_t q_dtype;
+    float softmax_scale;
+    int32_t max_partitions;
+    int32_t task_budget;
+    int32_t mxfp4_scaled_qk;
+} pa_problem;
+
+/* Opaque plan: validated problem, task list and partition workspace. */
+typedef struct pa_plan pa_plan_t;
+
+/* A HIP stream (hipStream_t); NULL means the default stream. */
+typedef void* pa_stream_t;
+
+/*
+ * pa_plan -- validate the problem, probe the device once per process (refuses
+ * anything but gfx950 with PA_ERR_UNSUPPORTED), cut every sequence into
+ * 256-token tiles and the tiles into partitions (PR #7092, "Root cause": only
+ * ceil(L/256) tiles per sequence exist; PR #7056, "Bandwidth": tile kernel plus
+ * partition reducer), and allocate the device workspace (task list, partition
+ * partials). The task list is copied to the device on `stream`.
+ *
+ * host_context_lens: optional host int32[num_seqs]. With it, partitions follow
+ * the real lengths (the device lengths passed to pa_decode must then be equal
+ * or shorter). Without it, every sequence is split as if it had
+ * max_context_len tokens and the kernels clamp to the device lengths.
+ *
+ * Ownership: *plan_out belongs to the caller; release it with pa_plan_destroy.
+ * Refusals: see pa_status. A host length above max_blocks_per_seq * page_size
+ * or above max_context_len is PA_ERR_INVALID_ARG.
+ */
+pa_status pa_plan(const pa_problem* problem, const int32_t* host_context_lens, pa_stream_t stream,
+                  pa_plan_t** plan_out);
+
+/*
+ * pa_decode -- enqueue the decode on `stream`: the tile kernel, then (when a
+ * sequence has more than one partition) the log-sum-exp merge kernel. It
+ * neither allocates nor synchronizes. Calls that share a plan must be
+ * stream-ordered, since the plan owns the partition workspace.
+ *
+ * All pointers are caller-owned device memory, 16-byte aligned:
+ *   query         [B][qlen][Hq][D]    bf16, or e4m3 bytes (PA_Q_FP8_E4M3)
+ *   key_cache     [num_blocks][Hkv][page][D] bf16 / e4m3; MXFP4: uint8 [..][page][D/2]
+ *   value_cache   like key_cache; TRANSPOSED: [num_blocks][Hkv][D][page]
+ *   k_scale, v_scale  NULL (bf16); fp32[1] (per-tensor); fp32 [num_blocks][Hkv][page]
+ *                 (per-token); MXFP4: uint8 e8m0 [num_blocks][Hkv][page][D/32]
+ *   block_tables  int32 [B][max_blocks_per_seq]
+ *   context_lens  int32 [B]
+ *   out           bf16 [B][qlen][Hq][D]; every element is written
+ *
+ * Device-side guarantees: block_tables columns >= ceil(L/page) are never read;
+ * tiles past ceil(L/256) are never read; tokens >= L never affect out; page ids
+ * outside [0, num_blocks) and lengths outside [0, max_blocks_per_seq * page]
+ * are clamped so that no access leaves the caller's buffers (the output of
+ * such a sequence is then unspecified).
+ */
+pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_cache, const void* value_cache,
+                    const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                    const int32_t* context_lens, void* out, pa_stream_t stream);
+
+/* Release a plan and its device workspace (NULL-safe). Synchronizes the device. */
+void pa_plan_destroy(pa_plan_t* plan);
+
+/* Device bytes owned by the plan (task list + partition partials). */
+size_t pa_plan_workspace_bytes(const pa_plan_t* plan);
+
+/* Plan summary for logging and tests. */
+typedef struct pa_plan_info {
+    int32_t num_tasks;        /* workgroups of the tile kernel */
+    int32_t max_parts;        /* largest partition count of any sequence */
+    int32_t total_parts;      /* partitions that write partials (sequences with > 1 partition) */
+    int32_t tiles_per_task;   /* target tiles per task the planner chose */
+    int32_t merge_needed;     /* 1 if pa_decode launches the merge kernel */
+    int32_t num_cus;          /* compute units the plan was sized for */
+} pa_plan_info;
+
+pa_status pa_plan_get_info(const pa_plan_t* plan, pa_plan_info* info);
+
+/*
+ * Host-only planner, for inspection and tests (no device needed). Fills
+ * tasks_out (int32 x 4 per task: b, kvh | part << 16, tile_begin, tile_end)
+ * and seq_parts_out (int32 x 2 per sequence: partitions, first partial slot or
+ * -1). Capacities are in records; *num_tasks receives the count (when the
+ * capacity is too small, nothing is written and PA_ERR_INVALID_ARG returns
+ * with *num_tasks set to the required capacity).
+ */
+pa_status pa_plan_host(const pa_problem* problem, const int32_t* host_context_lens, int32_t num_cus,
+                       int32_t* tasks_out, int32_t task_capacity, int32_t* num_tasks, int32_t* seq_parts_out,
+                       pa_plan_info* info);
+
+/*
+ * Per-kernel timing for measurement. With timing on, pa_decode records HIP
+ * events around each kernel it launches on the caller's stream (no
+ * allocation: the events are created here). pa_plan_read_timing waits for the
+ * recorded events, returns the summed durations in milliseconds and the number
+ * of calls, and clears the record. Not thread-safe; intended for benchmarks.
+ */
+pa_status pa_plan_set_timing(pa_plan_t* plan, int32_t enable, int32_t max_calls);
+pa_status pa_plan_read_timing(pa_plan_t* plan, double* tile_ms, double* merge_ms, int32_t* calls);
+
+/* Thread-local message of the last failure on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version string. */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,428 @@
+// Host side of libpa: C ABI, validation, device probe, planner and launches.
+//
+// The planner follows the work decomposition of ROCm/aiter PR #7092 ("Root
+// cause": a sequence has ceil(context_len / 256) tiles and no others) and the
+// partitioned plan of PR #7056 ("Microbench", "Bandwidth": tile kernel plus a
+// partition reducer, a default task budget of about two workgroups per
+// compute unit). Tiles of one (sequence, KV head) are cut into contiguous
+// partitions; each partition is one workgroup; tasks are launched longest
+// first so the ragged tail of the grid is short.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+struct DeviceInfo {
+    int device = -1;
+    int num_cus = 0;
+    bool gfx950 = false;
+    std::string arch;
+};
+
+std::mutex g_dev_mu;
+std::vector<DeviceInfo> g_devs;  // probed once per device per process
+
+pa_status probe_device(DeviceInfo* out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    for (const DeviceInfo& d : g_devs)
+        if (d.device == dev) {
+            *out = d;
+            return PA_OK;
+        }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    DeviceInfo d;
+    d.device = dev;
+    d.num_cus = prop.multiProcessorCount;
+    d.arch = prop.gcnArchName;
+    d.gfx950 = d.arch.compare(0, 6, "gfx950") == 0;
+    g_devs.push_back(d);
+    *out = d;
+    return PA_OK;
+}
+
+int rows_of(const pa_problem& p) { return p.qlen * p.q_per_kv; }
+
+pa_status validate(const pa_problem* p) {
+    if (!p) return fail(PA_ERR_INVALID_ARG, "problem is NULL");
+    if (p->num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
+    if (p->qlen < 1 || p->num_kv_heads < 1 || p->q_per_kv < 1)
+        return fail(PA_ERR_INVALID_ARG, "qlen, num_kv_heads and q_per_kv must be >= 1");
+    if (p->num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "num_kv_heads > 65535");
+    if (p->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1 (block 0 always exists)");
+    if (p->max_blocks_per_seq < 0 || p->max_context_len < 0)
+        return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq and max_context_len must be >= 0");
+    if (p->kv_dtype < PA_KV_BF16 || p->kv_dtype > PA_KV_MXFP4) return fail(PA_ERR_INVALID_ARG, "unknown kv_dtype");
+    if (p->scale_mode < PA_SCALE_NONE || p->scale_mode > PA_SCALE_PER_TOKEN)
+        return fail(PA_ERR_INVALID_ARG, "unknown scale_mode");
+    if (p->v_layout != PA_V_PLAIN && p->v_layout != PA_V_TRANSPOSED) return fail(PA_ERR_INVALID_ARG, "unknown v_layout");
+    if (p->q_dtype != PA_Q_BF16 && p->q_dtype != PA_Q_FP8_E4M3) return fail(PA_ERR_INVALID_ARG, "unknown q_dtype");
+    if (!(std::isfinite(p->softmax_scale))) return fail(PA_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (p->mxfp4_scaled_qk != 0 && p->mxfp4_scaled_qk != 1)
+        return fail(PA_ERR_INVALID_ARG, "mxfp4_scaled_qk must be 0 or 1");
+    if (p->max_partitions < 0 || p->task_budget < 0)
+        return fail(PA_ERR_INVALID_ARG, "max_partitions and task_budget must be >= 0");
+    if (p->page_size != 16 && p->page_size != 64 && p->page_size != 128)
+        return fail(PA_ERR_UNSUPPORTED, "page_size %d (supported: 16, 64, 128)", p->page_size);
+    if (p->head_dim != 128 && p->head_dim != 256)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 128, 256)", p->head_dim);
+    if (rows_of(*p) > 32)
+        return fail(PA_ERR_UNSUPPORTED, "qlen * q_per_kv = %d query rows per KV head (supported: <= 32)", rows_of(*p));
+    if ((long long)p->max_blocks_per_seq * p->page_size > (1LL << 30))
+        return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^30 tokens");
+    if (p->kv_dtype == PA_KV_BF16) {
+        if (p->scale_mode != PA_SCALE_NONE) return fail(PA_ERR_INVALID_ARG, "bf16 KV takes no scales (scale_mode NONE)");
+        if (p->q_dtype != PA_Q_BF16) return fail(PA_ERR_UNSUPPORTED, "bf16 KV needs a bf16 query");
+    } else if (p->kv_dtype == PA_KV_FP8_E4M3) {
+        if (p->scale_mode == PA_SCALE_NONE)
+            return fail(PA_ERR_INVALID_ARG, "fp8 KV needs per-tensor or per-token scales");
+        if (p->q_dtype != PA_Q_BF16) return fail(PA_ERR_UNSUPPORTED, "fp8 KV needs a bf16 query");
+    } else {
+        // MXFP4 (PR #7056, "Summary": head_dim 128, block size 128, query_length 1,
+        // up to 16 query heads per KV head; no transposed V)
+        if (p->scale_mode != PA_SCALE_NONE)
+            return fail(PA_ERR_INVALID_ARG, "MXFP4 carries its own e8m0 block scales (scale_mode NONE)");
+        if (p->page_size != 128) return fail(PA_ERR_UNSUPPORTED, "MXFP4 needs page_size 128");
+        if (p->head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "MXFP4 needs head_dim 128");
+        if (p->qlen != 1) return fail(PA_ERR_UNSUPPORTED, "MXFP4 needs qlen 1");
+        if (p->q_per_kv > 16) return fail(PA_ERR_UNSUPPORTED, "MXFP4 supports up to 16 query heads per KV head");
+        if (p->v_layout != PA_V_PLAIN) return fail(PA_ERR_UNSUPPORTED, "MXFP4 needs the plain V layout");
+    }
+    return PA_OK;
+}
+
+pa::KernelKey key_of(const pa_problem& p) {
+    pa::KernelKey k;
+    k.kv = p.kv_dtype == PA_KV_BF16 ? pa::KV_BF16 : (p.kv_dtype == PA_KV_FP8_E4M3 ? pa::KV_FP8 : pa::KV_MXFP4);
+    k.scale = p.scale_mode == PA_SCALE_NONE ? pa::SC_NONE : (p.scale_mode == PA_SCALE_PER_TENSOR ? pa::SC_TENSOR : pa::SC_TOKEN);
+    k.vt = p.v_layout == PA_V_TRANSPOSED ? 1 : 0;
+    k.head_dim = p.head_dim;
+    k.page = p.page_size;
+    k.ntiles_n = rows_of(p) <= 16 ? 1 : 2;
+    k.q_fp8 = p.q_dtype == PA_Q_FP8_E4M3 ? 1 : 0;
+    k.mx_scaled = (p.kv_dtype == PA_KV_MXFP4 && p.mxfp4_scaled_qk) ? 1 : 0;
+    return k;
+}
+
+struct Plan {
+    std::vector<int32_t> tasks;      // 4 per task
+    std::vector<int32_t> seq_parts;  // 2 per sequence
+    pa_plan_info info{};
+};
+
+// Cut every (sequence, KV head) into partitions of contiguous tiles.
+pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, Plan* out) {
+    const int B = p.num_seqs, H = p.num_kv_heads;
+    const int max_parts = p.max_partitions > 0 ? std::min(p.max_partitions, 65535) : 64;
+    const int budget = p.task_budget > 0 ? p.task_budget : std::max(1, 2 * num_cus);
+    const long cap_tokens = (long)p.max_blocks_per_seq * p.page_size;
+    std::vector<int> tiles(B);
+    for (int b = 0; b < B; ++b) {
+        long L = lens ? lens[b] : p.max_context_len;
+        if (lens) {
+            if (L < 0) return fail(PA_ERR_INVALID_ARG, "context_lens[%d] = %ld < 0", b, L);
+            if (L > cap_tokens)
+                return fail(PA_ERR_INVALID_ARG, "context_lens[%d] = %ld exceeds max_blocks_per_seq * page_size = %ld", b,
+                            L, cap_tokens);
+            if (L > p.max_context_len)
+                return fail(PA_ERR_INVALID_ARG, "context_lens[%d] = %ld exceeds max_context_len = %d", b, L,
+                            p.max_context_len);
+        } else {
+            L = std::min(L, cap_tokens);
+        }
+        tiles[b] = (int)((L + pa::kTileTokens - 1) / pa::kTileTokens);
+    }
+    long work = 0;
+    for (int b = 0; b < B; ++b) work += (long)tiles[b] * H;
+    const int tpt = (int)std::max<long>(1, (work + budget - 1) / budget);  // target tiles per task
+    out->tasks.clear();
+    out->seq_parts.assign(2 * (size_t)B, 0);
+    int slot = 0, maxp = 0;
+    for (int b = 0; b < B; ++b) {
+        int P = std::max(1, std::min(max_parts, (tiles[b] + tpt - 1) / tpt));
+        maxp = std::max(maxp, P);
+        out->seq_parts[2 * b] = P;
+        out->seq_parts[2 * b + 1] = P > 1 ? slot : -1;
+        if (P > 1) slot += P;
+        for (int kvh = 0; kvh < H; ++kvh)
+            for (int part = 0; part < P; ++part) {
+                const int t0 = (int)((long)part * tiles[b] / P), t1 = (int)((long)(part + 1) * tiles[b] / P);
+                out->tasks.insert(out->tasks.end(), {b, kvh | (part << 16), t0, t1});
+            }
+    }
+    // longest first; ties keep (sequence, head, partition) order
+    const size_t n = out->tasks.size() / 4;
+    std::vector<size_t> order(n);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) {
+        return out->tasks[4 * x + 3] - out->tasks[4 * x + 2] > out->tasks[4 * y + 3] - out->tasks[4 * y + 2];
+    });
+    std::vector<int32_t> sorted(out->tasks.size());
+    for (size_t i = 0; i < n; ++i)
+        for (int k = 0; k < 4; ++k) sorted[4 * i + k] = out->tasks[4 * order[i] + k];
+    out->tasks.swap(sorted);
+    if (n > 0x7FFFFFFF / 4) return fail(PA_ERR_UNSUPPORTED, "too many tasks");
+    out->info.num_tasks = (int32_t)n;
+    out->info.max_parts = maxp;
+    out->info.total_parts = slot;
+    out->info.tiles_per_task = tpt;
+    out->info.merge_needed = slot > 0 ? 1 : 0;
+    out->info.num_cus = num_cus;
+    return PA_OK;
+}
+
+}  // namespace
+
+struct pa_plan {
+    pa_problem prob{};
+    pa::KernelKey key{};
+    pa_plan_info info{};
+    int device = -1;
+    int32_t* d_tasks = nullptr;
+    int32_t* d_seq_parts = nullptr;
+    float* d_part_ml = nullptr;
+    float* d_part_o = nullptr;
+    size_t ws_bytes = 0;
+    // timing
+    bool timing = false;
+    int max_calls = 0;
+    mutable int ncalls = 0;
+    std::vector<hipEvent_t> ev;  // 3 per call
+};
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+const char* pa_version(void) { return "pa_decode gfx950 0.1"; }
+
+pa_status pa_plan_host(const pa_problem* problem, const int32_t* host_context_lens, int32_t num_cus,
+                       int32_t* tasks_out, int32_t task_capacity, int32_t* num_tasks, int32_t* seq_parts_out,
+                       pa_plan_info* info) {
+    pa_status st = validate(problem);
+    if (st != PA_OK) return st;
+    if (num_cus < 1) return fail(PA_ERR_INVALID_ARG, "num_cus must be >= 1");
+    Plan plan;
+    st = build_plan(*problem, host_context_lens, num_cus, &plan);
+    if (st != PA_OK) return st;
+    if (num_tasks) *num_tasks = plan.info.num_tasks;
+    if (info) *info = plan.info;
+    if (tasks_out) {
+        if (task_capacity < plan.info.num_tasks) return fail(PA_ERR_INVALID_ARG, "task capacity too small");
+        std::memcpy(tasks_out, plan.tasks.data(), plan.tasks.size() * sizeof(int32_t));
+    }
+    if (seq_parts_out) std::memcpy(seq_parts_out, plan.seq_parts.data(), plan.seq_parts.size() * sizeof(int32_t));
+    return PA_OK;
+}
+
+pa_status pa_plan(const pa_problem* problem, const int32_t* host_context_lens, pa_stream_t stream,
+                  pa_plan_t** plan_out) {
+    if (!plan_out) return fail(PA_ERR_INVALID_ARG, "plan_out is NULL");
+    *plan_out = nullptr;
+    pa_status st = validate(problem);
+    if (st != PA_OK) return st;
+    DeviceInfo dev;
+    st = probe_device(&dev);
+    if (st != PA_OK) return st;
+    if (!dev.gfx950) return fail(PA_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 only", dev.device, dev.arch.c_str());
+    const pa::KernelKey key = key_of(*problem);
+    if (!pa::have_tile_kernel(key)) return fail(PA_ERR_UNSUPPORTED, "no kernel instance for this problem");
+    Plan plan;
+    st = build_plan(*problem, host_context_lens, dev.num_cus, &plan);
+    if (st != PA_OK) return st;
+
+    pa_plan_t* p = new (std::nothrow) pa_plan_t();
+    if (!p) return fail(PA_ERR_OOM, "host allocation failed");
+    p->prob = *problem;
+    p->key = key;
+    p->info = plan.info;
+    p->device = dev.device;
+    const size_t rows = (size_t)rows_of(*problem);
+    const size_t nslots = (size_t)plan.info.total_parts * problem->num_kv_heads * rows;
+    const size_t tasks_b = std::max<size_t>(16, plan.tasks.size() * sizeof(int32_t));
+    const size_t seq_b = std::max<size_t>(16, plan.seq_parts.size() * sizeof(int32_t));
+    const size_t ml_b = std::max<size_t>(16, nslots * 2 * sizeof(float));
+    const size_t o_b = std::max<size_t>(16, nslots * problem->head_dim * sizeof(float));
+    hipError_t e;
+    if ((e = hipMalloc(&p->d_tasks, tasks_b)) != hipSuccess || (e = hipMalloc(&p->d_seq_parts, seq_b)) != hipSuccess ||
+        (e = hipMalloc(&p->d_part_ml, ml_b)) != hipSuccess || (e = hipMalloc(&p->d_part_o, o_b)) != hipSuccess) {
+        pa_plan_destroy(p);
+        return fail(PA_ERR_OOM, "workspace allocation failed: %s", hipGetErrorString(e));
+    }
+    p->ws_bytes = tasks_b + seq_b + ml_b + o_b;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!plan.tasks.empty() &&
+        (e = hipMemcpyAsync(p->d_tasks, plan.tasks.data(), plan.tasks.size() * sizeof(int32_t), hipMemcpyHostToDevice, s)) !=
+            hipSuccess) {
+        pa_plan_destroy(p);
+        return fail(PA_ERR_HIP, "task upload failed: %s", hipGetErrorString(e));
+    }
+    if (!plan.seq_parts.empty() &&
+        (e = hipMemcpyAsync(p->d_seq_parts, plan.seq_parts.data(), plan.seq_parts.size() * sizeof(int32_t),
+                            hipMemcpyHostToDevice, s)) != hipSuccess) {
+        pa_plan_destroy(p);
+        return fail(PA_ERR_HIP, "partition table upload failed: %s", hipGetErrorString(e));
+    }
+    // the host vectors die with this call: make the uploads complete first
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) {
+        pa_plan_destroy(p);
+        return fail(PA_ERR_HIP, "plan upload sync failed: %s", hipGetErrorString(e));
+    }
+    if (std::getenv("PA_LOG"))
+        std::fprintf(stderr, "[pa] plan: %d tasks, %d tiles/task target, max %d partitions, %d partial slots, %zu B workspace\n",
+                     plan.info.num_tasks, plan.info.tiles_per_task, plan.info.max_parts, plan.info.total_parts, p->ws_bytes);
+    *plan_out = p;
+    return PA_OK;
+}
+
+void pa_plan_destroy(pa_plan_t* p) {
+    if (!p) return;
+    if (p->d_tasks || p->d_seq_parts || p->d_part_ml || p->d_part_o || !p->ev.empty()) (void)hipDeviceSynchronize();
+    if (p->d_tasks) (void)hipFree(p->d_tasks);
+    if (p->d_seq_parts) (void)hipFree(p->d_seq_parts);
+    if (p->d_part_ml) (void)hipFree(p->d_part_ml);
+    if (p->d_part_o) (void)hipFree(p->d_part_o);
+    for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
+    delete p;
+}
+
+size_t pa_plan_workspace_bytes(const pa_plan_t* p) { return p ? p->ws_bytes : 0; }
+
+pa_status pa_plan_get_info(const pa_plan_t* p, pa_plan_info* info) {
+    if (!p || !info) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    *info = p->info;
+    return PA_OK;
+}
+
+static bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_cache, const void* value_cache,
+                    const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                    const int32_t* context_lens, void* out, pa_stream_t stream) {
+    if (!plan) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+    const pa_problem& p = plan->prob;
+    if (p.num_seqs == 0) return PA_OK;
+    if (!query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+        return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (misaligned(query) || misaligned(key_cache) || misaligned(value_cache) || misaligned(out))
+        return fail(PA_ERR_INVALID_ARG, "query, caches and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return fail(PA_ERR_INVALID_ARG, "block_tables and context_lens must be 4-byte aligned");
+    const bool need_scales = p.kv_dtype == PA_KV_MXFP4 || p.scale_mode != PA_SCALE_NONE;
+    if (need_scales && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale are required");
+    if (need_scales && (misaligned(k_scale) || misaligned(v_scale)) &&
+        !(p.scale_mode == PA_SCALE_PER_TENSOR && !((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u)))
+        return fail(PA_ERR_INVALID_ARG, "scale tables must be 16-byte aligned (per-tensor scales: 4-byte)");
+    hipError_t e = hipSetDevice(plan->device);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipSetDevice failed: %s", hipGetErrorString(e));
+
+    pa::TileArgs a;
+    a.q = query;
+    a.k = key_cache;
+    a.v = value_cache;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.tasks = plan->d_tasks;
+    a.seq_parts = plan->d_seq_parts;
+    a.part_ml = plan->d_part_ml;
+    a.part_o = plan->d_part_o;
+    a.num_seqs = p.num_seqs;
+    a.qlen = p.qlen;
+    a.num_kv_heads = p.num_kv_heads;
+    a.q_per_kv = p.q_per_kv;
+    a.rows = rows_of(p);
+    a.max_blocks = p.max_blocks_per_seq;
+    a.num_blocks = p.num_blocks;
+    const double sm = p.softmax_scale != 0.f ? (double)p.softmax_scale : 1.0 / std::sqrt((double)p.head_dim);
+    a.scale_log2 = (float)(sm * 1.4426950408889634);
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    pa_plan_t* mp = const_cast<pa_plan_t*>(plan);
+    const bool rec = mp->timing && mp->ncalls < mp->max_calls;
+    hipEvent_t* ev = rec ? &mp->ev[3 * (size_t)mp->ncalls] : nullptr;
+    if (rec && (e = hipEventRecord(ev[0], s)) != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    e = pa::launch_tile(plan->key, a, plan->info.num_tasks, s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "tile kernel launch failed: %s", hipGetErrorString(e));
+    if (rec && (e = hipEventRecord(ev[1], s)) != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    if (plan->info.merge_needed) {
+        e = pa::launch_merge(a, p.head_dim, s);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
+    }
+    if (rec) {
+        if ((e = hipEventRecord(ev[2], s)) != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+        mp->ncalls++;
+    }
+    return PA_OK;
+}
+
+pa_status pa_plan_set_timing(pa_plan_t* p, int32_t enable, int32_t max_calls) {
+    if (!p) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+    if (enable && max_calls < 1) return fail(PA_ERR_INVALID_ARG, "max_calls must be >= 1");
+    p->ncalls = 0;
+    p->timing = enable != 0;
+    if (!enable) return PA_OK;
+    hipError_t e = hipSetDevice(p->device);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipSetDevice failed: %s", hipGetErrorString(e));
+    while ((int)p->ev.size() < 3 * max_calls) {
+        hipEvent_t ev;
+        if ((e = hipEventCreate(&ev)) != hipSuccess) return fail(PA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+        p->ev.push_back(ev);
+    }
+    p->max_calls = max_calls;
+    return PA_OK;
+}
+
+pa_status pa_plan_read_timing(pa_plan_t* p, double* tile_ms, double* merge_ms, int32_t* calls) {
+    if (!p) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+    double t = 0, m = 0;
+    for (int i = 0; i < p->ncalls; ++i) {
+        hipEvent_t* ev = &p->ev[3 * (size_t)i];
+        hipError_t e = hipEventSynchronize(ev[2]);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+        float a = 0, b = 0;
+        if ((e = hipEventElapsedTime(&a, ev[0], ev[1])) != hipSuccess ||
+            (e = hipEventElapsedTime(&b, ev[1], ev[2])) != hipSuccess)
+            return fail(PA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+        t += a;
+        m += b;
+    }
+    if (tile_ms) *tile_ms = t;
+    if (merge_ms) *merge_ms = m;
+    if (calls) *calls = p->ncalls;
+    p->ncalls = 0;
+    return PA_OK;
+}
+
+}  // extern "C"

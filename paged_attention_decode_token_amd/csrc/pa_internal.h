@@ -1,0 +1,51 @@
+// Internal interface between the host side (pa_api.cpp) and the kernels
+// (pa_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum KvKind { KV_BF16 = 0, KV_FP8 = 1, KV_MXFP4 = 2 };
+enum ScaleKind { SC_NONE = 0, SC_TENSOR = 1, SC_TOKEN = 2 };
+
+// Tokens per planning tile: the unit of work per sequence (ROCm/aiter PR #7092,
+// "Root cause": ceil(context_len / 256) tiles per sequence).
+constexpr int kTileTokens = 256;
+// Threads per workgroup of the tile kernel: four 64-wide waves, each owning
+// 64 tokens of every tile (PR #7056, "Behavior and intent").
+constexpr int kTileThreads = 256;
+
+struct TileArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* ks;  // per-tensor fp32[1], per-token fp32 table, or MXFP4 e8m0 bytes
+    const void* vs;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    void* out;                 // bf16 [B][qlen][Hq][D]
+    const int32_t* tasks;      // int32 x 4 per task
+    const int32_t* seq_parts;  // int32 x 2 per sequence: partitions, first partial slot
+    float* part_ml;            // [slots][Hkv][rows][2]: running max (base 2), sum of weights
+    float* part_o;             // [slots][Hkv][rows][D]: unnormalised weighted sum of V
+    int32_t num_seqs, qlen, num_kv_heads, q_per_kv, rows, max_blocks, num_blocks;
+    float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct KernelKey {
+    int kv, scale, vt, head_dim, page, ntiles_n, q_fp8, mx_scaled;
+};
+
+// Launch the tile kernel for `key` (returns hipErrorInvalidValue for a key with
+// no compiled instance).
+hipError_t launch_tile(const KernelKey& key, const TileArgs& args, int num_tasks, hipStream_t stream);
+
+// Launch the cross-partition log-sum-exp merge for every output row.
+hipError_t launch_merge(const TileArgs& args, int head_dim, hipStream_t stream);
+
+// Whether an instance exists for `key`.
+bool have_tile_kernel(const KernelKey& key);
+
+}  // namespace pa

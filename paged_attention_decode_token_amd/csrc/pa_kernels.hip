@@ -1,0 +1,849 @@
+// Paged-attention decode kernels for gfx950 (MI355X).
+//
+// Tile kernel: one workgroup per task (sequence b, KV head, partition = a
+// contiguous range of 256-token tiles; ROCm/aiter PR #7092, "Root cause").
+// Four waves split every tile into 64-token slices and keep a wave-private
+// online softmax (running max m, weight sum l, accumulator O) over their
+// slices, with no barrier in the tile loop; the four waves merge once at the
+// end (ROCm/aiter PR #7056, "Behavior and intent").
+//
+// Per 64-token slice and wave:
+//   QK  S^T[token][row] = K . Q^T on v_mfma_f32_16x16x32_bf16 (bf16 cache; an
+//       e4m3 cache is widened to bf16 exactly), or on the block-scaled
+//       v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 K (e8m0 scale per 32) and
+//       e4m3 Q for an MXFP4 cache (PR #7056, "Summary").
+//   softmax in base 2, row max across the wave with cross-lane shuffles.
+//   PV  O^T[d][row] += V^T . P^T on the bf16 MFMA, P rounded to bf16. Token-
+//       major V goes through a wave-private LDS tile and is read back
+//       transposed with ds_read_b64_tr_b16; a transposed V feeds the MFMA
+//       straight from its loads.
+// Only the last, partial tile of a sequence runs the masked variant
+// (PR #7092, "Fix"): scores of tokens >= L become -inf by a select, and V
+// bytes and per-token scales of those tokens are zeroed before the PV
+// product, so 0 * NaN can never reach the accumulator. Tiles past
+// ceil(L/256) and table columns past ceil(L/page) are never read; page slots
+// of the boundary tile beyond the last owned page read block 0 and are
+// masked like any other unowned row.
+//
+// Merge kernel: per output row, combines the partitions' (m, l, O) with a
+// log-sum-exp weighting in a fixed partition order and writes bf16.
+//
+// Lane layouts of the matrix instructions used here (measured on gfx950):
+//   16x16x32 bf16: A lane (m, g) holds A[m][8g..8g+7], B lane (n, g) holds
+//     B[8g..8g+7][n], C lane (n, g) holds C[4g..4g+3][n]  (m, n = lane % 16,
+//     g = lane / 16).
+//   16x16x128 f8f6f4 with fp4 A: A lane (m, g) nibble i (element 2i in the
+//     low nibble) is k = 32g + i; an fp8 B lane (n, g) byte j is
+//     k = 16g + j for j < 16 and k = 64 + 16g + (j - 16) for j >= 16; the
+//     scale byte of lane group g applies to k in [32g, 32g + 32) on both
+//     operands (the placement PR #7056 describes for its fold).
+//   ds_read_b64_tr_b16: within each 16-lane group, output lane i element e
+//     comes from source lane 4e + i/4, element i % 4.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define PA_DEV __device__ __forceinline__
+
+// ------------------------------------------------------------------ helpers
+
+PA_DEV u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+PA_DEV u32x2 ld8(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
+PA_DEV uint32_t ld4(const char* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+PA_DEV int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+PA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+PA_DEV float shfl_xor(float v, int mask) {
+    int lane = __lane_id();
+    int src = lane ^ mask;
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+PA_DEV uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+PA_DEV float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+PA_DEV float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Two e4m3 bytes (selected 16-bit half of w) -> two bf16 (exact: every e4m3
+// value is a bf16 value).
+template <bool HI>
+PA_DEV uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+// Four e4m3 bytes -> four bf16 in two dwords.
+PA_DEV u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    u32x2 r;
+    r[0] = fp8x2_to_bf16x2<false>(w);
+    r[1] = fp8x2_to_bf16x2<true>(w);
+    return r;
+}
+// Eight e4m3 bytes -> bf16x8 fragment.
+PA_DEV bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    u32x2 a = fp8x4_to_bf16x4(w0), b = fp8x4_to_bf16x4(w1);
+    u32x4 r = {a[0], a[1], b[0], b[1]};
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// e8m0 byte -> fp32 2^(byte - 127) (byte 0 gives the subnormal 2^-127).
+PA_DEV float e8m0_to_f32(uint32_t byte) {
+    return byte == 0 ? __builtin_bit_cast(float, 0x00400000u) : __builtin_bit_cast(float, byte << 23);
+}
+
+// Eight e2m1 values (one dword, element 2i in the low nibble of byte i) times
+// `scale` -> bf16x8 (exact for the scales an e8m0 byte in [1, 254] encodes
+// times any e2m1 value).
+template <int SEL>
+PA_DEV uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL);
+    return __builtin_bit_cast(uint32_t, r);
+}
+PA_DEV u32x4 fp4x8_to_bf16x8(uint32_t w, float scale) {
+    u32x4 r;
+    r[0] = fp4x2_to_bf16x2<0>(w, scale);
+    r[1] = fp4x2_to_bf16x2<1>(w, scale);
+    r[2] = fp4x2_to_bf16x2<2>(w, scale);
+    r[3] = fp4x2_to_bf16x2<3>(w, scale);
+    return r;
+}
+
+PA_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+PA_DEV f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Byte mask keeping the first `valid` bytes (valid clamped to 0..4) of a dword.
+PA_DEV uint32_t keep_bytes(int valid) {
+    valid = valid < 0 ? 0 : (valid > 4 ? 4 : valid);
+    return valid >= 4 ? 0xFFFFFFFFu : ((1u << (8 * valid)) - 1u);
+}
+
+// ----------------------------------------------------------- configuration
+
+template <int KV_, int SC_, int VT_, int D_, int PG_, int NT_, int QF8_, int MXS_>
+struct Cfg {
+    static constexpr int KV = KV_;
+    static constexpr int SC = SC_;
+    static constexpr bool VT = VT_ != 0;
+    static constexpr int D = D_;
+    static constexpr int PG = PG_;
+    static constexpr int NT = NT_;  // 16-row N tiles of query rows (rows <= 16 * NT)
+    static constexpr bool QF8 = QF8_ != 0;
+    // MXFP4 QK on the block-scaled fp4 x fp8 MFMA (fast) instead of exact
+    // widening of K to bf16 and the bf16 MFMA (default). On gfx950 the scaled
+    // instruction sums some operand mixes to only about 2^-13 of their largest
+    // product, which near-tied logits turn into output errors above the
+    // element bound; the widened form is exact up to fp32 accumulation.
+    static constexpr bool MXS = KV_ == KV_MXFP4 && MXS_ != 0;
+    // P enters PV as bf16 hi + lo parts (two MFMAs) for MXFP4: its softmax is
+    // near one-hot and its V rows reach 6 * 2^9, so bf16 rounding of a
+    // runner-up weight alone would move an output element by far more than the
+    // element bound wherever the mixed V rows cancel
+    static constexpr bool PSPLIT = KV == KV_MXFP4;
+    static constexpr int ESZ = KV == KV_BF16 ? 2 : 1;                // bytes per bf16/fp8 element
+    static constexpr int ROWB = KV == KV_MXFP4 ? D / 2 : D * ESZ;    // bytes of one token row (data)
+    static constexpr int SROWB = KV == KV_MXFP4 ? D / 32 : 0;        // bytes of one token's e8m0 scales
+    static constexpr int KSTEPS = D / 32;                            // bf16 MFMA k-steps per 16 tokens
+    static constexpr int KLOADS = KV == KV_MXFP4 ? 1 : ROWB / 64;    // 16-byte K loads per lane per call
+    static constexpr int DT = D / 16;                                // 16-wide d tiles of O
+    static constexpr int NPC = PG >= 64 ? 1 : 64 / PG;               // pages per 64-token slice
+    static constexpr long PAGE_BYTES_HEAD = (long)PG * ROWB;         // one (page, head) of K or V data
+    // token-major V staged through LDS, one 32-token PV step at a time, bf16
+    static constexpr bool STAGE_V = !VT;
+    static constexpr int VPITCH = D * 2 + 16;                        // LDS row pitch in bytes
+    static constexpr int VSTAGE_BYTES = STAGE_V ? 32 * VPITCH : 0;   // per wave
+    static constexpr int ROWS_PAD = 16 * NT;
+    static constexpr int OPITCH = D + 4;                             // floats
+    static constexpr int EPI_BYTES = 2 * ROWS_PAD * OPITCH * 4 + 2 * 4 * ROWS_PAD * 4;
+    static constexpr int SMEM = (4 * VSTAGE_BYTES > EPI_BYTES) ? 4 * VSTAGE_BYTES : EPI_BYTES;
+    // staging geometry for token-major V loads
+    static constexpr int LPR = ROWB / 16;         // lanes per token row
+    static constexpr int TPI = 64 / LPR;          // tokens per load instruction
+    static constexpr int IPS = 32 / TPI;          // load instructions per 32-token step
+};
+
+template <class C>
+struct State {
+    f32x4 o[C::DT][C::NT];  // O^T[16dt + 4g + j][16nt + n]
+    float m[C::NT];         // running max of the row, base-2 logits
+    float l[C::NT];         // running sum of weights (this lane's tokens only)
+};
+
+struct Ctx {
+    int b, kvh, L, npages, lane, ln, lg, wave;
+    const int32_t* bt_row;
+    const char* kbase;   // K data of this head in page 0
+    const char* vbase;   // V data of this head in page 0
+    const char* ksbase;  // per-token / MXFP4 scales of this head in page 0
+    const char* vsbase;
+    float kscale;        // per-tensor K scale (1 otherwise)
+};
+
+// Query fragments (B operand of QK).
+template <class C>
+struct QFrag {
+    bf16x8 q[C::NT][C::KSTEPS];  // bf16 B operand (bf16 / fp8 caches, exact MXFP4 QK)
+    i32x8 q8[C::NT];             // e4m3 B operand of the scaled MXFP4 QK
+    int qsc[C::NT];              // its e8m0 scale byte (2^e of the query row)
+};
+
+// d index held at position 0 of the bf16 Q/K fragment for k-step ks, lane group g.
+template <class C>
+PA_DEV int kfrag_d0(int ks, int g) {
+    if (C::KV == KV_BF16)
+        return 32 * ks + 8 * g;
+    return 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);  // fp8: one 16-byte load feeds two k-steps
+}
+
+template <class C>
+PA_DEV void load_q(const TileArgs& a, const Ctx& cx, QFrag<C>& qf) {
+    const int Hq = a.num_kv_heads * a.q_per_kv;
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+        const int r = 16 * nt + cx.ln;
+        const bool valid = r < a.rows;
+        const int rr = valid ? r : 0;
+        const long row = ((long)cx.b * a.qlen + rr / a.q_per_kv) * Hq + (long)cx.kvh * a.q_per_kv + rr % a.q_per_kv;
+        if constexpr (C::KV != KV_MXFP4) {
+            const char* qp = reinterpret_cast<const char*>(a.q) + row * C::D * 2;
+#pragma unroll
+            for (int ks = 0; ks < C::KSTEPS; ++ks) {
+                u32x4 v = ld16(qp + 2 * kfrag_d0<C>(ks, cx.lg));
+                if (!valid) v = u32x4{0, 0, 0, 0};
+                qf.q[nt][ks] = as_bf16x8(v);
+            }
+        } else {
+            // MXFP4: this lane's 32 query elements as e4m3 bytes. Scaled QK
+            // wants d = 16g + [0,16) then 64 + 16g + [0,16) (the fp8 B layout of
+            // the 16x16x128 scaled MFMA); exact QK wants d = 32g + [0,32).
+            auto pos = [&](int j) -> int {
+                if constexpr (C::MXS) return j < 16 ? 16 * cx.lg + j : 64 + 16 * cx.lg + (j - 16);
+                return 32 * cx.lg + j;
+            };
+            uint32_t bytes[8];
+            int e = 0;
+            if constexpr (C::QF8) {
+                // e4m3 query used as stored, unit scale
+                const char* qp = reinterpret_cast<const char*>(a.q) + row * C::D;
+                u32x4 lo = ld16(qp + pos(0)), hi = ld16(qp + pos(16));
+                if (!valid) { lo = u32x4{0, 0, 0, 0}; hi = lo; }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) { bytes[k] = lo[k]; bytes[4 + k] = hi[k]; }
+            } else {
+                // bf16 query row quantized to e4m3 with a power-of-two scale 2^e,
+                // e the smallest integer with max|q| <= 448 * 2^e (0 for a zero row)
+                const char* qp = reinterpret_cast<const char*>(a.q) + row * C::D * 2;
+                float x[32];
+                u32x4 w[4] = {ld16(qp + 2 * pos(0)), ld16(qp + 2 * pos(8)), ld16(qp + 2 * pos(16)), ld16(qp + 2 * pos(24))};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        uint32_t d = valid ? w[k][j] : 0u;
+                        x[8 * k + 2 * j] = bf16_lo(d);
+                        x[8 * k + 2 * j + 1] = bf16_hi(d);
+                    }
+                float amax = 0.f;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+                amax = fmaxf(amax, shfl_xor(amax, 16));
+                amax = fmaxf(amax, shfl_xor(amax, 32));
+                if (amax > 0.f) {
+                    int ex;
+                    float fr = frexpf(amax, &ex);  // amax = fr * 2^ex, fr in [0.5, 1)
+                    e = (fr <= 0.875f) ? ex - 9 : ex - 8;
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    float f0 = ldexpf(x[4 * k + 0], -e), f1 = ldexpf(x[4 * k + 1], -e);
+                    float f2 = ldexpf(x[4 * k + 2], -e), f3 = ldexpf(x[4 * k + 3], -e);
+                    int t = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);  // round to nearest even
+                    bytes[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, t, true);
+                }
+            }
+            if constexpr (C::MXS) {
+                qf.q8[nt] = i32x8{(int)bytes[0], (int)bytes[1], (int)bytes[2], (int)bytes[3],
+                                  (int)bytes[4], (int)bytes[5], (int)bytes[6], (int)bytes[7]};
+                const int sb = 127 + e;
+                qf.qsc[nt] = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
+            } else {
+                // widen qhat * 2^e to bf16 (exact): k-step s holds d = 32g + 8s + [0, 8)
+                const float qs = ldexpf(1.0f, e);
+#pragma unroll
+                for (int st = 0; st < C::KSTEPS; ++st) {
+                    u32x4 v;
+                    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)bytes[2 * st], qs, false));
+                    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)bytes[2 * st], qs, true));
+                    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)bytes[2 * st + 1], qs, false));
+                    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)bytes[2 * st + 1], qs, true));
+                    qf.q[nt][st] = as_bf16x8(v);
+                }
+            }
+        }
+    }
+}
+
+// Page id of table slot `slot` (pinned to block 0 past the owned pages and
+// clamped into the pool).
+template <bool MASK>
+PA_DEV int page_of(const TileArgs& a, const Ctx& cx, int slot) {
+    int p = 0;
+    if (!MASK || slot < cx.npages) p = cx.bt_row[slot];
+    p = p < 0 ? 0 : (p >= a.num_blocks ? a.num_blocks - 1 : p);
+    return p;
+}
+
+// One 64-token slice [cb, cb + 64) of one wave.
+template <class C, bool MASK>
+PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>& st, int cb, char* vlds) {
+    constexpr int D = C::D, PG = C::PG, NT = C::NT;
+    const int ln = cx.ln, lg = cx.lg, lane = cx.lane;
+
+    // ---- pages of this slice. pg[q] (uniform) is only ever indexed with
+    // compile-time q; lanes whose page depends on the lane read the table.
+    int pg[C::NPC];
+#pragma unroll
+    for (int q = 0; q < C::NPC; ++q) pg[q] = uniform(page_of<MASK>(a, cx, cb / PG + q));
+    const int inoff = (PG > 64) ? (cb % PG) : 0;  // slice offset inside its page (PG = 128)
+    // slot inside its page of slice token t (t in [0, 64))
+    auto slot_of = [&](int t) -> int { return C::NPC == 1 ? inoff + t : (t & (PG - 1)); };
+    // page of a per-lane slice token t
+    auto lane_page = [&](int t) -> int { return C::NPC == 1 ? pg[0] : page_of<MASK>(a, cx, cb / PG + t / PG); };
+
+    // ---- K loads: lane (m = ln, g = lg), call c holds token 16*(ln>>2) + 4c + (ln&3)
+    const int ktok0 = 16 * (ln >> 2) + (ln & 3);
+    const int kpage = lane_page(ktok0);
+    const char* krow = cx.kbase + (long)kpage * a.num_kv_heads * C::PAGE_BYTES_HEAD +
+                       (long)slot_of(ktok0) * C::ROWB;
+    u32x4 kr[4][C::KLOADS];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int u = 0; u < C::KLOADS; ++u) kr[c][u] = ld16(krow + 4 * c * C::ROWB + 64 * u + 16 * lg);
+    uint32_t ksc[4];
+    if constexpr (C::KV == KV_MXFP4) {
+        const char* srow = cx.ksbase + (long)kpage * a.num_kv_heads * PG * C::SROWB +
+                           (long)slot_of(ktok0) * C::SROWB;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ksc[c] = (ld4(srow + 4 * c * C::SROWB) >> (8 * lg)) & 0xFFu;
+    }
+
+    // ---- per-token scales of this lane's score/P tokens 16*lg + [0, 16)
+    float tks[16], tvs[16];
+    if constexpr (C::SC == SC_TOKEN) {
+        const int t0 = 16 * lg;
+        const long off = ((long)lane_page(t0) * a.num_kv_heads * PG + slot_of(t0)) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4 kv4 = ld16(cx.ksbase + off + 16 * i), vv4 = ld16(cx.vsbase + off + 16 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // element first, then reinterpret: bit-casting a vector
+                // element expression directly yields element 0 with this clang
+                const uint32_t kw = kv4[j], vw = vv4[j];
+                tks[4 * i + j] = __builtin_bit_cast(float, kw);
+                tvs[4 * i + j] = __builtin_bit_cast(float, vw);
+            }
+        }
+        if (MASK) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const bool ok = cb + t0 + i < cx.L;
+                tks[i] = ok ? tks[i] : 0.f;
+                tvs[i] = ok ? tvs[i] : 0.f;
+            }
+        }
+    }
+
+    // ---- V loads
+    // token-major: step s stages slice tokens 16*(e>>3) + 8s + (e&7), e in [0, 32)
+    u32x4 vr[2][C::IPS];
+    uint32_t vsc[2][C::IPS];
+    const int vseg = lane % C::LPR;
+    if constexpr (C::STAGE_V) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < C::IPS; ++i) {
+                const int e = i * C::TPI + lane / C::LPR;
+                const int t = 16 * (e >> 3) + 8 * s + (e & 7);
+                // page of token t: e >> 3 is the same for every lane of instruction i
+                const int vpage = pg[C::NPC == 1 ? 0 : ((i * C::TPI) >> 3) * 16 / PG];
+                const long row = (long)vpage * a.num_kv_heads * PG + slot_of(t);
+                vr[s][i] = ld16(cx.vbase + row * C::ROWB + 16 * vseg);
+                if constexpr (C::KV == KV_MXFP4) vsc[s][i] = (ld4(cx.vsbase + row * C::SROWB) >> (8 * vseg)) & 0xFFu;
+            }
+    }
+    // transposed: lane (d = 16dt + ln, lg) holds slice tokens 16*lg + [0, 16) of row d
+    constexpr int VTW = C::VT ? (C::ESZ == 2 ? 2 : 1) : 0;  // 16-byte loads per d tile
+    u32x4 vt[C::VT ? C::DT : 1][VTW > 0 ? VTW : 1];
+    if constexpr (C::VT) {
+        const int t0 = 16 * lg;
+        const char* vcol = cx.vbase + (long)lane_page(t0) * a.num_kv_heads * C::PAGE_BYTES_HEAD +
+                           (long)slot_of(t0) * C::ESZ;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int w = 0; w < VTW; ++w) vt[dt][w] = ld16(vcol + (long)(16 * dt + ln) * PG * C::ESZ + 16 * w);
+        if (MASK) {
+            // keep only the bytes of tokens < L (byte-granular, PR #7092 "Fix")
+            const int valid = cx.L - (cb + t0);  // tokens of this lane's 16 that are owned
+#pragma unroll
+            for (int w = 0; w < VTW; ++w)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int first = (16 * w + 4 * j) / C::ESZ;  // first token of this dword
+                    uint32_t mk = keep_bytes((valid - first) * C::ESZ);
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) vt[dt][w][j] &= mk;
+                }
+        }
+    }
+
+    // ---- QK: S^T[token][row]; acc[c][nt][j] <-> slice token 16*lg + 4c + j, row 16nt + ln
+    f32x4 acc[4][NT];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (C::MXS) {
+                i32x8 ka = {(int)kr[c][0][0], (int)kr[c][0][1], (int)kr[c][0][2], (int)kr[c][0][3], 0, 0, 0, 0};
+                s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf.q8[nt], s, 4, 0, 0, (int)ksc[c], 0,
+                                                                     qf.qsc[nt]);
+            } else if constexpr (C::KV == KV_MXFP4) {
+                // K widened exactly: dword st holds d = 32g + 8st + [0, 8) times its block scale
+                const float ksf = e8m0_to_f32(ksc[c]);
+#pragma unroll
+                for (int st = 0; st < C::KSTEPS; ++st)
+                    s = mfma_bf16(as_bf16x8(fp4x8_to_bf16x8(kr[c][0][st], ksf)), qf.q[nt][st], s);
+            } else if constexpr (C::KV == KV_BF16) {
+#pragma unroll
+                for (int ks = 0; ks < C::KSTEPS; ++ks) s = mfma_bf16(as_bf16x8(kr[c][ks]), qf.q[nt][ks], s);
+            } else {
+#pragma unroll
+                for (int u = 0; u < C::KLOADS; ++u) {
+                    s = mfma_bf16(fp8x8_to_bf16x8(kr[c][u][0], kr[c][u][1]), qf.q[nt][2 * u], s);
+                    s = mfma_bf16(fp8x8_to_bf16x8(kr[c][u][2], kr[c][u][3]), qf.q[nt][2 * u + 1], s);
+                }
+            }
+            acc[c][nt] = s;
+        }
+
+    // ---- scale, mask, online softmax (base 2), P^T fragments
+    const float sc = a.scale_log2 * cx.kscale;
+    u32x4 pf[2][NT];   // P^T B-operand for PV steps 0/1
+    u32x4 pfl[2][NT];  // low parts of P when PSPLIT
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float mloc = -__builtin_inff();
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * lg + 4 * c + j;
+                float x = acc[c][nt][j] * sc;
+                if constexpr (C::SC == SC_TOKEN) x *= tks[4 * c + j];
+                if (MASK) x = (cb + t < cx.L) ? x : -__builtin_inff();
+                acc[c][nt][j] = x;
+                mloc = fmaxf(mloc, x);
+            }
+        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+        const float mnew = fmaxf(st.m[nt], mloc);
+        const float muse = (mnew == -__builtin_inff()) ? 0.f : mnew;
+        const float alpha = fast_exp2(st.m[nt] - muse);
+        st.m[nt] = mnew;
+        float lsum = 0.f;
+        uint32_t pw[8], plo[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[j] = fast_exp2(acc[c][nt][j] - muse);
+            uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);
+            if constexpr (C::PSPLIT) {
+                plo[2 * c] = pack_bf16(p[0] - bf16_lo(w0), p[1] - bf16_hi(w0));
+                plo[2 * c + 1] = pack_bf16(p[2] - bf16_lo(w1), p[3] - bf16_hi(w1));
+                lsum += (p[0] + p[1]) + (p[2] + p[3]);
+            } else {
+                lsum += (bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1));
+            }
+            if constexpr (C::SC == SC_TOKEN) {
+                w0 = pack_bf16(bf16_lo(w0) * tvs[4 * c + 0], bf16_hi(w0) * tvs[4 * c + 1]);
+                w1 = pack_bf16(bf16_lo(w1) * tvs[4 * c + 2], bf16_hi(w1) * tvs[4 * c + 3]);
+            }
+            pw[2 * c] = w0;
+            pw[2 * c + 1] = w1;
+        }
+        st.l[nt] = st.l[nt] * alpha + lsum;
+        // step s uses calls 2s (tokens 16lg + 8s + 0..3) and 2s + 1 (16lg + 8s + 4..7)
+        pf[0][nt] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+        pf[1][nt] = u32x4{pw[4], pw[5], pw[6], pw[7]};
+        if constexpr (C::PSPLIT) {
+            pfl[0][nt] = u32x4{plo[0], plo[1], plo[2], plo[3]};
+            pfl[1][nt] = u32x4{plo[4], plo[5], plo[6], plo[7]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] *= alpha;
+    }
+
+    // ---- PV
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        if constexpr (C::STAGE_V) {
+            // stage rows e of step s into the wave's LDS tile (bf16, row pitch VPITCH)
+#pragma unroll
+            for (int i = 0; i < C::IPS; ++i) {
+                const int e = i * C::TPI + lane / C::LPR;
+                const int t = 16 * (e >> 3) + 8 * s + (e & 7);
+                const bool ok = !MASK || (cb + t < cx.L);
+                char* dst = vlds + e * C::VPITCH;
+                u32x4 raw = vr[s][i];
+                if constexpr (C::KV == KV_BF16) {
+                    if (!ok) raw = u32x4{0, 0, 0, 0};
+                    *reinterpret_cast<u32x4*>(dst + 16 * vseg) = raw;
+                } else if constexpr (C::KV == KV_FP8) {
+                    if (!ok) raw = u32x4{0, 0, 0, 0};
+                    u32x2 a0 = fp8x4_to_bf16x4(raw[0]), a1 = fp8x4_to_bf16x4(raw[1]);
+                    u32x2 a2 = fp8x4_to_bf16x4(raw[2]), a3 = fp8x4_to_bf16x4(raw[3]);
+                    *reinterpret_cast<u32x4*>(dst + 32 * vseg) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                    *reinterpret_cast<u32x4*>(dst + 32 * vseg + 16) = u32x4{a2[0], a2[1], a3[0], a3[1]};
+                } else {
+                    const float vsf = e8m0_to_f32(vsc[s][i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        u32x4 w = fp4x8_to_bf16x8(raw[j], vsf);
+                        if (!ok) w = u32x4{0, 0, 0, 0};
+                        *reinterpret_cast<u32x4*>(dst + 64 * vseg + 16 * j) = w;
+                    }
+                }
+            }
+            // staged rows are read back by other lanes of the same wave
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+            bf16x8 va;
+            if constexpr (C::STAGE_V) {
+                // A lane (m = d offset, g) needs rows 8g + [0, 8) at column 16dt + m
+                const char* base = vlds + (8 * lg + (ln >> 2)) * C::VPITCH + 2 * (16 * dt + 4 * (ln & 3));
+                bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(base));
+                bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(base + 4 * C::VPITCH));
+                va = bf16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+            } else if constexpr (C::ESZ == 2) {
+                va = as_bf16x8(vt[dt][s]);
+            } else {
+                va = fp8x8_to_bf16x8(vt[dt][0][2 * s], vt[dt][0][2 * s + 1]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pf[s][nt]), st.o[dt][nt]);
+                if constexpr (C::PSPLIT) st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pfl[s][nt]), st.o[dt][nt]);
+            }
+        }
+        if constexpr (C::STAGE_V) {
+            // the next step overwrites the tile: all lanes' reads must be done
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(kTileThreads) void pa_tile_kernel(const TileArgs a) {
+    constexpr int D = C::D, NT = C::NT, PG = C::PG;
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+
+    Ctx cx;
+    cx.lane = threadIdx.x & 63;
+    cx.wave = threadIdx.x >> 6;
+    cx.ln = cx.lane & 15;
+    cx.lg = cx.lane >> 4;
+    const int* task = a.tasks + 4 * blockIdx.x;
+    cx.b = uniform(task[0]);
+    const int kp = uniform(task[1]);
+    cx.kvh = kp & 0xFFFF;
+    const int part = kp >> 16;
+    const int tb = uniform(task[2]);
+    int L = uniform(a.context_lens[cx.b]);
+    L = L < 0 ? 0 : L;
+    L = L > a.max_blocks * PG ? a.max_blocks * PG : L;
+    cx.L = L;
+    const int ntiles = (L + kTileTokens - 1) / kTileTokens;
+    const int te = min(uniform(task[3]), ntiles);
+    cx.npages = (L + PG - 1) / PG;
+    cx.bt_row = a.block_tables + (long)cx.b * a.max_blocks;
+    const long head_bytes = C::PAGE_BYTES_HEAD;
+    cx.kbase = reinterpret_cast<const char*>(a.k) + (long)cx.kvh * head_bytes;
+    cx.vbase = reinterpret_cast<const char*>(a.v) + (long)cx.kvh * head_bytes;
+    cx.kscale = 1.f;
+    float vscale = 1.f;
+    if constexpr (C::SC == SC_TENSOR) {
+        cx.kscale = *reinterpret_cast<const float*>(a.ks);
+        vscale = *reinterpret_cast<const float*>(a.vs);
+    }
+    if constexpr (C::SC == SC_TOKEN) {
+        cx.ksbase = reinterpret_cast<const char*>(a.ks) + (long)cx.kvh * PG * 4;
+        cx.vsbase = reinterpret_cast<const char*>(a.vs) + (long)cx.kvh * PG * 4;
+    } else if constexpr (C::KV == KV_MXFP4) {
+        cx.ksbase = reinterpret_cast<const char*>(a.ks) + (long)cx.kvh * PG * C::SROWB;
+        cx.vsbase = reinterpret_cast<const char*>(a.vs) + (long)cx.kvh * PG * C::SROWB;
+    } else {
+        cx.ksbase = cx.vsbase = nullptr;
+    }
+
+    QFrag<C> qf;
+    load_q<C>(a, cx, qf);
+
+    State<C> st;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        st.m[nt] = -__builtin_inff();
+        st.l[nt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    char* vlds = smem + cx.wave * C::VSTAGE_BYTES;
+    // full tiles: every token of the tile is owned
+    const int te_full = min(te, L / kTileTokens);
+    for (int tile = tb; tile < te_full; ++tile) slice<C, false>(a, cx, qf, st, tile * kTileTokens + 64 * cx.wave, vlds);
+    // the boundary tile (peeled): masked
+    if (te > te_full && te_full >= tb) {
+        const int cb = te_full * kTileTokens + 64 * cx.wave;
+        if (cb < L) slice<C, true>(a, cx, qf, st, cb, vlds);
+    }
+
+    // ---- merge the four waves (fixed order), then store
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        st.l[nt] += shfl_xor(st.l[nt], 16);
+        st.l[nt] += shfl_xor(st.l[nt], 32);
+    }
+    __syncthreads();  // V staging tiles are no longer needed
+    float* obuf = reinterpret_cast<float*>(smem);                              // [2][ROWS_PAD][OPITCH]
+    float* mbuf = obuf + 2 * C::ROWS_PAD * C::OPITCH;                          // [4][ROWS_PAD]
+    float* lbuf = mbuf + 4 * C::ROWS_PAD;                                      // [4][ROWS_PAD]
+    if (cx.lg == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            mbuf[cx.wave * C::ROWS_PAD + 16 * nt + cx.ln] = st.m[nt];
+            lbuf[cx.wave * C::ROWS_PAD + 16 * nt + cx.ln] = st.l[nt];
+        }
+    }
+    __syncthreads();
+    float Mrow[NT], Lrow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + cx.ln;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, mbuf[w * C::ROWS_PAD + r]);
+        float Lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float mw = mbuf[w * C::ROWS_PAD + r];
+            Lt += (M == -__builtin_inff()) ? 0.f : fast_exp2(mw - M) * lbuf[w * C::ROWS_PAD + r];
+        }
+        const float f = (M == -__builtin_inff()) ? 0.f : fast_exp2(st.m[nt] - M);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] *= f;
+        Mrow[nt] = M;
+        Lrow[nt] = Lt;
+    }
+    auto obuf_at = [&](int buf, int nt, int dt) -> float* {
+        return obuf + (buf * C::ROWS_PAD + 16 * nt + cx.ln) * C::OPITCH + 16 * dt + 4 * cx.lg;
+    };
+    if (cx.wave >= 2) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(obuf_at(cx.wave - 2, nt, dt)) = st.o[dt][nt];
+    }
+    __syncthreads();
+    if (cx.wave < 2) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] += *reinterpret_cast<f32x4*>(obuf_at(cx.wave, nt, dt));
+    }
+    __syncthreads();
+    if (cx.wave == 1) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(obuf_at(0, nt, dt)) = st.o[dt][nt];
+    }
+    __syncthreads();
+    if (cx.wave != 0) return;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] += *reinterpret_cast<f32x4*>(obuf_at(0, nt, dt));
+
+    const int nparts = a.seq_parts[2 * cx.b];
+    const int Hq = a.num_kv_heads * a.q_per_kv;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + cx.ln;
+        if (r >= a.rows) continue;
+        if (nparts <= 1) {
+            const float inv = (Lrow[nt] > 0.f) ? vscale / Lrow[nt] : 0.f;
+            const long orow = ((long)cx.b * a.qlen + r / a.q_per_kv) * Hq + (long)cx.kvh * a.q_per_kv + r % a.q_per_kv;
+            char* op = reinterpret_cast<char*>(a.out) + orow * D * 2;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                const f32x4 o = st.o[dt][nt];
+                u32x2 w = {pack_bf16(o[0] * inv, o[1] * inv), pack_bf16(o[2] * inv, o[3] * inv)};
+                *reinterpret_cast<u32x2*>(op + 2 * (16 * dt + 4 * cx.lg)) = w;
+            }
+        } else {
+            const long slot = (long)a.seq_parts[2 * cx.b + 1] + part;
+            const long prow = (slot * a.num_kv_heads + cx.kvh) * a.rows + r;
+            float* po = a.part_o + prow * D;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * cx.lg) = st.o[dt][nt] * vscale;
+            if (cx.lg == 0) {
+                a.part_ml[2 * prow] = Mrow[nt];
+                a.part_ml[2 * prow + 1] = Lrow[nt];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- merge kernel
+
+// One wave per output row (b, i, h) of a sequence with more than one
+// partition: M = max_p m_p, w_p = 2^(m_p - M), out = sum_p w_p O_p / sum_p w_p l_p
+// in partition order (PR #7056, "Bandwidth": the partition reducer).
+template <int D>
+__global__ __launch_bounds__(256) void pa_merge_kernel(const TileArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int Hq = a.num_kv_heads * a.q_per_kv;
+    const long total = (long)a.num_seqs * a.qlen * Hq;
+    const long R = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (R >= total) return;
+    const int b = (int)(R / ((long)a.qlen * Hq));
+    const int rem = (int)(R % ((long)a.qlen * Hq));
+    const int i = rem / Hq, h = rem % Hq;
+    const int kvh = h / a.q_per_kv;
+    const int r = i * a.q_per_kv + h % a.q_per_kv;
+    const int P = a.seq_parts[2 * b];
+    if (P <= 1) return;
+    const long slot0 = a.seq_parts[2 * b + 1];
+    constexpr int PER = D / 64;
+    float M = -__builtin_inff();
+    for (int p = 0; p < P; ++p) M = fmaxf(M, a.part_ml[2 * (((slot0 + p) * a.num_kv_heads + kvh) * a.rows + r)]);
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+    float den = 0.f;
+    if (M != -__builtin_inff()) {
+        for (int p = 0; p < P; ++p) {
+            const long prow = ((slot0 + p) * a.num_kv_heads + kvh) * a.rows + r;
+            const float w = fast_exp2(a.part_ml[2 * prow] - M);
+            den += w * a.part_ml[2 * prow + 1];
+            const float* po = a.part_o + prow * D + PER * lane;
+            if constexpr (PER == 2) {
+                f32x2 v = *reinterpret_cast<const f32x2*>(po);
+                acc[0] += w * v[0];
+                acc[1] += w * v[1];
+            } else {
+                f32x4 v = *reinterpret_cast<const f32x4*>(po);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) acc[k] += w * v[k];
+            }
+        }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    char* op = reinterpret_cast<char*>(a.out) + R * D * 2 + 2 * PER * lane;
+    if constexpr (PER == 2) {
+        *reinterpret_cast<uint32_t*>(op) = pack_bf16(acc[0] * inv, acc[1] * inv);
+    } else {
+        *reinterpret_cast<u32x2*>(op) = u32x2{pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
+    }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+using TileFn = void (*)(const TileArgs);
+
+struct Entry {
+    KernelKey key;
+    TileFn fn;
+};
+
+#define PA_E(KV, SC, VT, D, PG, NT, QF) PA_EM(KV, SC, VT, D, PG, NT, QF, 0)
+#define PA_EM(KV, SC, VT, D, PG, NT, QF, MXS) \
+    {{KV, SC, VT, D, PG, NT, QF, MXS}, &pa_tile_kernel<Cfg<KV, SC, VT, D, PG, NT, QF, MXS>>}
+#define PA_PG(KV, SC, VT, D, NT) PA_E(KV, SC, VT, D, 16, NT, 0), PA_E(KV, SC, VT, D, 64, NT, 0), PA_E(KV, SC, VT, D, 128, NT, 0)
+#define PA_NT(KV, SC, VT, D) PA_PG(KV, SC, VT, D, 1), PA_PG(KV, SC, VT, D, 2)
+#define PA_D(KV, SC, VT) PA_NT(KV, SC, VT, 128), PA_NT(KV, SC, VT, 256)
+#define PA_VT(KV, SC) PA_D(KV, SC, 0), PA_D(KV, SC, 1)
+
+static const Entry kEntries[] = {
+    PA_VT(KV_BF16, SC_NONE),
+    PA_VT(KV_FP8, SC_TENSOR),
+    PA_VT(KV_FP8, SC_TOKEN),
+    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 0, 0),
+    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 1, 0),
+    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 0, 1),
+    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 1, 1),
+};
+
+static TileFn find(const KernelKey& k) {
+    for (const Entry& e : kEntries)
+        if (e.key.kv == k.kv && e.key.scale == k.scale && e.key.vt == k.vt && e.key.head_dim == k.head_dim &&
+            e.key.page == k.page && e.key.ntiles_n == k.ntiles_n && e.key.q_fp8 == k.q_fp8 &&
+            e.key.mx_scaled == k.mx_scaled)
+            return e.fn;
+    return nullptr;
+}
+
+bool have_tile_kernel(const KernelKey& key) { return find(key) != nullptr; }
+
+hipError_t launch_tile(const KernelKey& key, const TileArgs& args, int num_tasks, hipStream_t stream) {
+    TileFn fn = find(key);
+    if (!fn) return hipErrorInvalidValue;
+    if (num_tasks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fn, dim3(num_tasks), dim3(kTileThreads), 0, stream, args);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const TileArgs& args, int head_dim, hipStream_t stream) {
+    const long rows = (long)args.num_seqs * args.qlen * args.num_kv_heads * args.q_per_kv;
+    if (rows <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((rows + 3) / 4);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(pa_merge_kernel<128>, dim3(blocks), dim3(256), 0, stream, args);
+    else if (head_dim == 256)
+        hipLaunchKernelGGL(pa_merge_kernel<256>, dim3(blocks), dim3(256), 0, stream, args);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -283,44 +283,8 @@ def make_case(spec: Spec, fill: Optional[str] = None, seed: Optional[int] = None
     else:
         raise ValueError(spec.kv_dtype)
 
-    # unowned (page, slot) pairs: all of block 0, then every last-page tail
-    pages = [torch.zeros(PG, dtype=torch.int64)]
-    slots = [torch.arange(PG, dtype=torch.int64)]
-    for b in range(B):
-        L = lens[b]
-        if L > 0 and L % PG != 0:
-            last = int(bt[b, npages[b] - 1])
-            s = torch.arange(L % PG, PG, dtype=torch.int64)
-            pages.append(torch.full_like(s, last))
-            slots.append(s)
-    up = torch.cat(pages)
-    us = torch.cat(slots)
-    n_un = int(up.numel())
-    gp = torch.Generator().manual_seed(seed + 7919)  # poison stream, independent of the owned content
-
-    def poison_rows(t: torch.Tensor, kind: str):
-        # t: [num_blocks, H, PG] or [num_blocks, H, PG, X], all in token-major layout
-        store = t.view(torch.int16) if kind == "bf16" else t
-        if t.dim() == 3:
-            store[up, :, us] = _poison_value(kind, fill, gp, n_un * H).view(n_un, H)
-        else:
-            X = t.shape[3]
-            store[up, :, us, :] = _poison_value(kind, fill, gp, n_un * H * X).view(n_un, H, X)
-
-    if spec.kv_dtype == "bf16":
-        poison_rows(K, "bf16")
-        poison_rows(V, "bf16")
-    elif spec.kv_dtype == "fp8":
-        poison_rows(K, "u8")
-        poison_rows(V, "u8")
-        if spec.scale_mode == "token":
-            poison_rows(k_scale, "f32")
-            poison_rows(v_scale, "f32")
-    else:
-        poison_rows(K, "u8")
-        poison_rows(V, "u8")
-        poison_rows(k_scale, "e8m0")
-        poison_rows(v_scale, "e8m0")
+    K, V, k_scale, v_scale = _apply_fill(spec.kv_dtype, spec.scale_mode, K, V, k_scale, v_scale, bt, lens, PG,
+                                         fill, seed)
     if spec.v_layout == "trans":
         V = V.transpose(2, 3).contiguous()  # [num_blocks, H, D, PG]
 
@@ -329,6 +293,72 @@ def make_case(spec: Spec, fill: Optional[str] = None, seed: Optional[int] = None
                 kv_dtype=spec.kv_dtype, scale_mode=spec.scale_mode, v_layout=spec.v_layout, q_dtype=spec.q_dtype,
                 softmax_scale=0.0, query=query, key_cache=K, value_cache=V, k_scale=k_scale, v_scale=v_scale,
                 block_tables=bt, context_lens=torch.tensor(lens, dtype=torch.int32))
+
+
+def _unowned_pairs(bt, lens, PG):
+    """(pages, slots) of every row no sequence owns: all of block 0, then the
+    tail of each sequence's last page."""
+    pages = [torch.zeros(PG, dtype=torch.int64)]
+    slots = [torch.arange(PG, dtype=torch.int64)]
+    for b, L in enumerate(lens):
+        if L > 0 and L % PG != 0:
+            last = int(bt[b, (L + PG - 1) // PG - 1])
+            s = torch.arange(L % PG, PG, dtype=torch.int64)
+            pages.append(torch.full_like(s, last))
+            slots.append(s)
+    return torch.cat(pages), torch.cat(slots)
+
+
+def _apply_fill(kv_dtype, scale_mode, K, V, k_scale, v_scale, bt, lens, PG, fill, seed):
+    """Write `fill` into every unowned row of K, V (token-major) and their scales, in place."""
+    up, us = _unowned_pairs(bt, lens, PG)
+    n_un = int(up.numel())
+    H = K.shape[1]
+    gp = torch.Generator().manual_seed(seed + 7919)  # poison stream, independent of the owned content
+
+    def poison_rows(t: torch.Tensor, kind: str):
+        # t: [num_blocks, H, PG] or [num_blocks, H, PG, X]
+        store = t.view(torch.int16) if kind == "bf16" else t
+        if t.dim() == 3:
+            store[up, :, us] = _poison_value(kind, fill, gp, n_un * H).view(n_un, H)
+        else:
+            X = t.shape[3]
+            store[up, :, us, :] = _poison_value(kind, fill, gp, n_un * H * X).view(n_un, H, X)
+
+    if kv_dtype == "bf16":
+        poison_rows(K, "bf16")
+        poison_rows(V, "bf16")
+    elif kv_dtype == "fp8":
+        poison_rows(K, "u8")
+        poison_rows(V, "u8")
+        if scale_mode == "token":
+            poison_rows(k_scale, "f32")
+            poison_rows(v_scale, "f32")
+    else:
+        poison_rows(K, "u8")
+        poison_rows(V, "u8")
+        poison_rows(k_scale, "e8m0")
+        poison_rows(v_scale, "e8m0")
+    return K, V, k_scale, v_scale
+
+
+def refill(case: Case, fill: str, seed: Optional[int] = None) -> Case:
+    """A copy of `case` whose unowned rows hold `fill`; owned rows are identical."""
+    seed = case.spec.seed if seed is None else seed
+    K = case.key_cache.clone()
+    V = case.value_cache.clone()
+    trans = case.v_layout == "trans"
+    if trans:
+        V = V.transpose(2, 3).contiguous()
+    ks = None if case.k_scale is None else case.k_scale.clone()
+    vs = None if case.v_scale is None else case.v_scale.clone()
+    if case.kv_dtype == "fp8" and case.scale_mode == "tensor":
+        ks, vs = case.k_scale, case.v_scale
+    K, V, ks, vs = _apply_fill(case.kv_dtype, case.scale_mode, K, V, ks, vs, case.block_tables,
+                               case.context_lens.tolist(), case.page_size, fill, seed)
+    if trans:
+        V = V.transpose(2, 3).contiguous()
+    return dataclasses.replace(case, key_cache=K, value_cache=V, k_scale=ks, v_scale=vs)
 
 
 def owned_mask(case: Case) -> torch.Tensor:

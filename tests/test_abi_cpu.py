@@ -1,0 +1,128 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, validates descriptors, and the host planner covers every
+owned tile exactly once. No GPU is touched."""
+import os
+import re
+
+import pytest
+import torch
+
+from paged_attention_decode_token_amd import binding as B
+from paged_attention_decode_token_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:pa_status|void|size_t|const char\*)\s+(pa_\w+)\s*\(", src, re.M)))
+
+
+def test_header_symbols_are_exported():
+    lib = B.lib()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_version():
+    assert "gfx950" in B.pa_version()
+
+
+def _prob(**kw):
+    base = dict(num_seqs=4, qlen=1, num_kv_heads=2, q_per_kv=8, head_dim=128, page_size=16, num_blocks=100,
+                max_blocks_per_seq=40, max_context_len=600)
+    base.update(kw)
+    return B.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=32), B.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=64), B.PA_ERR_UNSUPPORTED),
+    (dict(qlen=5, q_per_kv=8), B.PA_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), B.PA_ERR_INVALID_ARG),
+    (dict(qlen=0), B.PA_ERR_INVALID_ARG),
+    (dict(kv_dtype="fp8"), B.PA_ERR_INVALID_ARG),  # fp8 without scales
+    (dict(kv_dtype="bf16", scale_mode="tensor"), B.PA_ERR_INVALID_ARG),
+    (dict(kv_dtype="mxfp4", page_size=64), B.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype="mxfp4", page_size=128, head_dim=256), B.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype="mxfp4", page_size=128, qlen=2), B.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype="mxfp4", page_size=128, q_per_kv=32), B.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype="mxfp4", page_size=128, v_layout="trans"), B.PA_ERR_UNSUPPORTED),
+    (dict(q_dtype="fp8"), B.PA_ERR_UNSUPPORTED),  # e4m3 query only with MXFP4
+    (dict(softmax_scale=float("nan")), B.PA_ERR_INVALID_ARG),
+])
+def test_refusals(kw, status):
+    with pytest.raises(B.PaError) as ei:
+        B.pa_plan_host(_prob(**kw), [10, 20, 30, 40])
+    assert ei.value.status == status
+    assert B.pa_last_error()
+
+
+def test_host_length_checks():
+    with pytest.raises(B.PaError):
+        B.pa_plan_host(_prob(), [10, -1, 30, 40])
+    with pytest.raises(B.PaError):  # longer than the table can address
+        B.pa_plan_host(_prob(max_context_len=10 ** 6), [10, 20, 30, 40 * 16 + 1])
+    with pytest.raises(B.PaError):  # longer than max_context_len
+        B.pa_plan_host(_prob(), [10, 20, 30, 601])
+
+
+@pytest.mark.parametrize("lens,budget,maxp", [
+    ([0, 1, 255, 256, 257, 600], 0, 0),
+    ([600] * 6, 0, 0),
+    ([1, 600, 33, 0, 599, 512], 1000, 0),
+    ([600, 600, 600, 600, 600, 600], 1000, 2),
+    ([5000] * 3 + [1], 0, 0),
+])
+def test_planner_covers_every_owned_tile_once(lens, budget, maxp):
+    n = len(lens)
+    p = _prob(num_seqs=n, max_blocks_per_seq=400, max_context_len=max(lens), task_budget=budget,
+              max_partitions=maxp)
+    tasks, parts, info = B.pa_plan_host(p, lens, num_cus=16)
+    H = p.num_kv_heads
+    seen = {}
+    for b, kp, t0, t1 in tasks.tolist():
+        kvh, part = kp & 0xFFFF, kp >> 16
+        assert 0 <= b < n and 0 <= kvh < H and 0 <= t0 <= t1
+        assert part < parts[b, 0]
+        for t in range(t0, t1):
+            key = (b, kvh, t)
+            assert key not in seen, key
+            seen[key] = part
+    for b, L in enumerate(lens):
+        nt = (L + 255) // 256
+        for kvh in range(H):
+            for t in range(nt):
+                assert (b, kvh, t) in seen
+        assert all(t < nt for (bb, _, t) in seen if bb == b)
+        # every (b, kvh) has exactly parts[b,0] tasks, partials only when split
+        cnt = sum(1 for r in tasks.tolist() if r[0] == b and (r[1] & 0xFFFF) == 0)
+        assert cnt == parts[b, 0]
+        assert (parts[b, 1] >= 0) == (parts[b, 0] > 1)
+    # longest first
+    sizes = (tasks[:, 3] - tasks[:, 2]).tolist()
+    assert sizes == sorted(sizes, reverse=True)
+    if maxp:
+        assert int(parts[:, 0].max()) <= maxp
+    assert info.num_tasks == len(tasks)
+
+
+def test_planner_without_host_lengths_uses_max_context():
+    p = _prob(num_seqs=3, max_context_len=1000, max_blocks_per_seq=100, task_budget=12)
+    tasks, parts, info = B.pa_plan_host(p, None, num_cus=16)
+    assert int(parts[:, 0].min()) == int(parts[:, 0].max())
+    assert int(tasks[:, 3].max()) == 4  # ceil(1000/256)
+
+
+def test_full_workload_plans():
+    for spec in I.FULL:
+        case_lens = I._lens(spec, torch.Generator().manual_seed(spec.seed))
+        PG = spec.page_size
+        width = max((L + PG - 1) // PG for L in case_lens) + 2
+        p = B.make_problem(spec.num_seqs, spec.qlen, spec.num_kv_heads, spec.q_per_kv, spec.head_dim, PG, 10,
+                           width, max(case_lens), spec.kv_dtype, spec.scale_mode, spec.v_layout, spec.q_dtype)
+        tasks, parts, info = B.pa_plan_host(p, case_lens, num_cus=256)
+        assert info.num_tasks >= 1 and info.max_parts <= 64

@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar (the survey's reading of the target): rel-L2 = ||gpu - o|| / ||o|| <= 3e-3
+over the compared rows, and |gpu_i - o_i| <= 2e-2 * max(1, |o_i|) per element,
+where o is the oracle's unrounded fp64 result and gpu is the bf16 output. Plus
+the NaN contract: output finite and bit-identical between runs whose unowned
+rows are zero-filled and runs where they hold NaN / Inf / random bytes
+(ROCm/aiter PR #7092, section "Tests"), and bit-identical across repeated runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_attention_decode_token_amd import binding as B
+from paged_attention_decode_token_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 3e-3
+ELEM = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()  # raises when libpa.so is missing
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy()
+
+
+def check_parity(gpu_out, ref, seqs=None, what=""):
+    g = gpu_out.float().cpu().double().numpy()
+    if seqs is not None:
+        g, ref = g[seqs], ref[seqs]
+    assert np.isfinite(g).all(), "%s: non-finite output" % what
+    err = g - ref
+    nrm = np.linalg.norm(ref)
+    rel = np.linalg.norm(err) / nrm if nrm > 0 else np.linalg.norm(err)
+    bound = ELEM * np.maximum(1.0, np.abs(ref))
+    worst = float((np.abs(err) / bound).max()) if err.size else 0.0
+    print("%s: rel-L2 %.3e, worst |err|/bound %.3f" % (what, rel, worst))
+    assert rel <= REL_L2, "%s: rel-L2 %.3e > %.1e" % (what, rel, REL_L2)
+    assert worst <= 1.0, "%s: element error %.3f x bound" % (what, worst)
+    return rel
+
+
+def run(case, **over):
+    out, plan = B.decode_case(case, **over)
+    torch.cuda.synchronize()
+    return out, plan
+
+
+SMALL = [I.small(s) for s in I.FULL if not s.name.endswith("l131072_qfp8") and not s.name.endswith("l131072_qbf16")]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_parity_small(spec):
+    case = I.make_case(spec)
+    ref = oracle.pa_decode(case)
+    out, plan = run(case)
+    check_parity(out, ref, what=spec.name)
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_poison_fills_are_bit_identical_to_zero_fill(spec):
+    case = I.make_case(spec, fill="zero")
+    ref_bits = _bits(run(case)[0])
+    assert np.isfinite(run(case)[0].float().cpu().numpy()).all()
+    for fill in ("nan", "inf", "random"):
+        out = run(I.refill(case, fill))[0]
+        assert np.array_equal(_bits(out), ref_bits), "%s fill changes the output" % fill
+
+
+@pytest.mark.parametrize("spec", SMALL[:3] + SMALL[5:6], ids=lambda s: s.name)
+def test_repeat_runs_are_bit_identical(spec):
+    case = I.make_case(spec)
+    d = B.device_tensors(case)
+    plan = B.pa_plan(B.problem_of(case), case.context_lens)
+    outs = []
+    for _ in range(3):
+        o = torch.full((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), float("nan"),
+                       dtype=torch.bfloat16, device="cuda")
+        B.pa_decode(plan, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
+                    d["block_tables"], d["context_lens"], o)
+        outs.append(_bits(o))
+    assert all(np.array_equal(o, outs[0]) for o in outs[1:])
+
+
+@pytest.mark.parametrize("spec", [SMALL[1], SMALL[3], SMALL[5], SMALL[6]], ids=lambda s: s.name)
+@pytest.mark.parametrize("variant", ["one_partition", "many_partitions", "no_host_lens"])
+def test_plan_variants_agree_with_oracle(spec, variant):
+    case = I.make_case(spec)
+    ref = oracle.pa_decode(case)
+    if variant == "one_partition":
+        out, plan = run(case, max_partitions=1)
+        assert plan.info().merge_needed == 0
+    elif variant == "many_partitions":
+        out, plan = run(case, task_budget=100000)
+        assert plan.info().max_parts > 1 or int(case.context_lens.max()) <= 256
+    else:
+        d = B.device_tensors(case)
+        plan = B.pa_plan(B.problem_of(case), None)
+        out = torch.full((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), float("nan"),
+                         dtype=torch.bfloat16, device="cuda")
+        B.pa_decode(plan, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
+                    d["block_tables"], d["context_lens"], out)
+        torch.cuda.synchronize()
+    check_parity(out, ref, what="%s/%s" % (spec.name, variant))
+
+
+EDGE_LENS = (0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 767, 1000)
+
+
+@pytest.mark.parametrize("base", [I.TINY_BF16, I.BF16_P64, I.FP8TOK_Q4, I.FP8_TRANS, I.MXFP4_SHORT_QBF],
+                         ids=lambda s: s.name)
+def test_edge_lengths(base):
+    spec = base.replace(name=base.name + "_edges", num_seqs=len(EDGE_LENS), lens=("fixed", EDGE_LENS),
+                        num_kv_heads=min(base.num_kv_heads, 2))
+    case = I.make_case(spec)
+    ref = oracle.pa_decode(case)
+    for over in ({}, {"task_budget": 100000}):
+        out, _ = run(case, **over)
+        check_parity(out, ref, what="%s %s" % (spec.name, over))
+        z = out[0].float().cpu()  # L = 0 row is exactly zero
+        assert torch.all(z == 0)
+
+
+def test_rows_of_context_len_one_are_v_row_zero():
+    spec = I.TINY_BF16.replace(name="len1", lens=("fixed", (1, 1, 1, 1)))
+    case = I.make_case(spec)
+    out, _ = run(case)
+    for b in range(4):
+        p = int(case.block_tables[b, 0])
+        v0 = case.value_cache[p, 0, 0].view(torch.int16)
+        for h in range(case.num_q_heads):
+            assert torch.equal(out[b, 0, h].cpu().view(torch.int16), v0)
+
+
+# ------------------------------------------------------------- full sizes
+
+FULL_SAMPLE = {  # sequences the oracle recomputes at full size
+    "tiny_bf16_p16": None,
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("spec", I.FULL, ids=lambda s: s.name)
+def test_full_size_sampled_parity_and_poison(spec):
+    case = I.make_case(spec)
+    out, plan = run(case)
+    seqs = list(range(case.num_seqs)) if case.num_seqs <= 4 else [0, 1, case.num_seqs // 2, case.num_seqs - 1]
+    ref = oracle.pa_decode(case, seqs=seqs)
+    check_parity(out, ref, seqs=seqs, what=spec.name + " (sampled)")
+    assert torch.isfinite(out.float()).all()
+    zero = run(I.refill(case, "zero"))[0]
+    assert torch.equal(zero.view(torch.int16), out.view(torch.int16)), "poisoned != zero-filled at full size"
+
+
+@pytest.mark.parametrize("spec", [s for s in SMALL if s.kv_dtype == "mxfp4"], ids=lambda s: s.name)
+def test_mxfp4_scaled_qk_mode(spec):
+    """The opt-in block-scaled fp4 x fp8 MFMA QK: rel-L2 bar, finite, poison
+    invariant. Its per-element error is not bounded on near-tied logits (the
+    instruction's accumulation is coarser than fp32 on some operand mixes), so
+    only the aggregate bar applies to this mode."""
+    case = I.make_case(spec)
+    ref = oracle.pa_decode(case)
+    out, _ = run(case, mxfp4_scaled_qk=1)
+    g = out.float().cpu().double().numpy()
+    assert np.isfinite(g).all()
+    rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+    print("%s scaled QK: rel-L2 %.3e" % (spec.name, rel))
+    assert rel <= REL_L2
+    zero = run(I.refill(case, "zero"), mxfp4_scaled_qk=1)[0]
+    assert torch.equal(zero.view(torch.int16), out.view(torch.int16))
