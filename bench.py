@@ -64,13 +64,65 @@ def time_cpu_oracle(case, target_s=15.0):
     dt = time.perf_counter() - t0
     n = max(1, min(case.num_seqs, int(target_s / max(dt, 1e-3))))
     seqs = list(range(n))
+    reps = 0
     t0 = time.perf_counter()
-    oracle.pa_decode(case, seqs=seqs)
-    dt = time.perf_counter() - t0
-    nbytes = case.kv_bytes(seqs)
+    while True:  # whole passes over the sample until about target_s of CPU work
+        oracle.pa_decode(case, seqs=seqs)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s or reps >= 100:
+            break
+    nbytes = case.kv_bytes(seqs) * reps
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d sequences (%.0f MB of KV) of the page-64 variant, %.1f s" % (
-                n, case.num_seqs, nbytes / 1e6, dt)}
+            "sample": "%d of %d sequences of the page-64 variant, %d passes (%.0f MB of KV), %.1f s" % (
+                n, case.num_seqs, reps, nbytes / 1e6, dt)}
+
+
+def time_all(steps, warmup):
+    """us per pa_decode call and KV GB/s of every workload (inputs resident in HBM)."""
+    import torch
+
+    import paged_attention_decode_token_amd as pa
+    from paged_attention_decode_token_amd import inputs as I
+
+    rows = {}
+    for spec in I.FULL:
+        case = I.make_case(spec)
+        d = pa.device_tensors(case)
+        plan = pa.pa_plan(pa.problem_of(case), case.context_lens)
+        out = torch.empty((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+
+        def call():
+            pa.pa_decode(plan, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
+                         d["block_tables"], d["context_lens"], out)
+
+        for _ in range(warmup):
+            call()
+        plan.set_timing(True, steps)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        t_ms, m_ms, n = plan.read_timing()
+        plan.set_timing(False)
+        nbytes = case.kv_bytes()
+        inf = plan.info()
+        rows[spec.name] = {"us_per_call": round(ms * 1e3, 2), "tile_us": round(t_ms / n * 1e3, 2),
+                           "merge_us": round(m_ms / n * 1e3, 2), "kv_bytes": nbytes,
+                           "kv_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                           "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                           "tasks": inf.num_tasks, "slots": inf.slots, "partitions_max": inf.max_parts}
+        print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  tasks %5d slots %4d" % (
+            spec.name, ms * 1e3, nbytes / (ms * 1e-3) / 1e9, 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            inf.num_tasks, inf.slots), file=sys.stderr, flush=True)
+        del d, plan, out, case
+        torch.cuda.empty_cache()
+    return rows
 
 
 def main():
@@ -79,6 +131,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every workload (one pa_decode call each) and print a table to stderr")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter calibration)")
     args = ap.parse_args()
@@ -173,8 +227,12 @@ def main():
                      "kernel": "pa_tile_kernel (bf16, D 128, page 64 and 128)",
                      "algorithmic_bytes_per_step": tile_bytes},
     }
+    if args.all:
+        del variants
+        torch.cuda.empty_cache()
+        res["all_workloads"] = time_all(args.steps, args.warmup)
     if not args.no_cpu:
-        res["cpu_baseline"] = time_cpu_oracle(variants[0]["case"])
+        res["cpu_baseline"] = time_cpu_oracle(I.make_case(I.BF16_P64))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -86,7 +86,9 @@ typedef enum pa_q_dtype { PA_Q_BF16 = 0, PA_Q_FP8_E4M3 = 1 } pa_q_dtype;
  *   kv_dtype, scale_mode, v_layout, q_dtype   see the enums (MXFP4: PLAIN only)
  *   softmax_scale       0 -> 1/sqrt(head_dim)
  *   max_partitions      0 -> 64; upper bound of partitions per sequence
- *   task_budget         0 -> 2 * compute units; target number of workgroups
+ *   task_budget         0 -> automatic: the tiles-per-task target with the lowest
+ *                       estimated completion time when tasks run longest first
+ *                       on the resident workgroup slots; > 0: about this many tasks
  *   mxfp4_scaled_qk     MXFP4 only. 0 (default): K is widened exactly to bf16 and
  *                       QK runs on the bf16 MFMA. 1: QK runs on the block-scaled
  *                       fp4 x fp8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) with
@@ -181,12 +183,15 @@ typedef struct pa_plan_info {
     int32_t tiles_per_task;   /* target tiles per task the planner chose */
     int32_t merge_needed;     /* 1 if pa_decode launches the merge kernel */
     int32_t num_cus;          /* compute units the plan was sized for */
+    int32_t slots;            /* tile workgroups resident at once (compute units x occupancy) */
 } pa_plan_info;
 
 pa_status pa_plan_get_info(const pa_plan_t* plan, pa_plan_info* info);
 
 /*
- * Host-only planner, for inspection and tests (no device needed). Fills
+ * Host-only planner, for inspection and tests (no device needed): plans as
+ * pa_plan would for a device with num_cus compute units holding
+ * blocks_per_cu tile workgroups each. Fills
  * tasks_out (int32 x 4 per task: b, kvh | part << 16, tile_begin, tile_end)
  * and seq_parts_out (int32 x 2 per sequence: partitions, first partial slot or
  * -1). Capacities are in records; *num_tasks receives the count (when the
@@ -194,8 +199,8 @@ pa_status pa_plan_get_info(const pa_plan_t* plan, pa_plan_info* info);
  * with *num_tasks set to the required capacity).
  */
 pa_status pa_plan_host(const pa_problem* problem, const int32_t* host_context_lens, int32_t num_cus,
-                       int32_t* tasks_out, int32_t task_capacity, int32_t* num_tasks, int32_t* seq_parts_out,
-                       pa_plan_info* info);
+                       int32_t blocks_per_cu, int32_t* tasks_out, int32_t task_capacity, int32_t* num_tasks,
+                       int32_t* seq_parts_out, pa_plan_info* info);
 
 /*
  * Per-kernel timing for measurement. With timing on, pa_decode records HIP

@@ -44,7 +44,7 @@ class pa_problem(ctypes.Structure):
 
 class pa_plan_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "num_tasks", "max_parts", "total_parts", "tiles_per_task", "merge_needed", "num_cus")]
+        "num_tasks", "max_parts", "total_parts", "tiles_per_task", "merge_needed", "num_cus", "slots")]
 
 
 EXPORTS = ["pa_plan", "pa_decode", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
     L.pa_plan_get_info.restype = ctypes.c_int
     L.pa_plan_get_info.argtypes = [vp, P(pa_plan_info)]
     L.pa_plan_host.restype = ctypes.c_int
-    L.pa_plan_host.argtypes = [P(pa_problem), vp, i32, vp, i32, P(i32), vp, P(pa_plan_info)]
+    L.pa_plan_host.argtypes = [P(pa_problem), vp, i32, i32, vp, i32, P(i32), vp, P(pa_plan_info)]
     L.pa_plan_set_timing.restype = ctypes.c_int
     L.pa_plan_set_timing.argtypes = [vp, i32, i32]
     L.pa_plan_read_timing.restype = ctypes.c_int
@@ -203,17 +203,18 @@ def pa_decode(plan: Plan, query, key_cache, value_cache, k_scale, v_scale, block
     return out
 
 
-def pa_plan_host(problem: pa_problem, host_context_lens=None, num_cus: int = 256):
+def pa_plan_host(problem: pa_problem, host_context_lens=None, num_cus: int = 256, blocks_per_cu: int = 2):
     """Host-only planner: (tasks int32 [n, 4], seq_parts int32 [B, 2], info)."""
     lens_buf = None if host_context_lens is None else torch.as_tensor(host_context_lens, dtype=torch.int32).contiguous()
     n = ctypes.c_int32()
     info = pa_plan_info()
     lp = None if lens_buf is None else ctypes.c_void_p(lens_buf.data_ptr())
-    _check(lib().pa_plan_host(ctypes.byref(problem), lp, num_cus, None, 0, ctypes.byref(n), None, ctypes.byref(info)))
+    _check(lib().pa_plan_host(ctypes.byref(problem), lp, num_cus, blocks_per_cu, None, 0, ctypes.byref(n), None,
+                              ctypes.byref(info)))
     tasks = torch.zeros((max(1, n.value), 4), dtype=torch.int32)
     parts = torch.zeros((max(1, problem.num_seqs), 2), dtype=torch.int32)
-    _check(lib().pa_plan_host(ctypes.byref(problem), lp, num_cus, ctypes.c_void_p(tasks.data_ptr()), n.value,
-                              ctypes.byref(n), ctypes.c_void_p(parts.data_ptr()), ctypes.byref(info)))
+    _check(lib().pa_plan_host(ctypes.byref(problem), lp, num_cus, blocks_per_cu, ctypes.c_void_p(tasks.data_ptr()),
+                              n.value, ctypes.byref(n), ctypes.c_void_p(parts.data_ptr()), ctypes.byref(info)))
     return tasks[:n.value], parts[:problem.num_seqs], info
 
 

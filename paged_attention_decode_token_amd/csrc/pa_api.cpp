@@ -16,7 +16,9 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <functional>
 #include <numeric>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -91,6 +93,7 @@ pa_status validate(const pa_problem* p) {
         return fail(PA_ERR_INVALID_ARG, "mxfp4_scaled_qk must be 0 or 1");
     if (p->max_partitions < 0 || p->task_budget < 0)
         return fail(PA_ERR_INVALID_ARG, "max_partitions and task_budget must be >= 0");
+    if (p->max_partitions > 64) return fail(PA_ERR_UNSUPPORTED, "max_partitions %d (supported: <= 64)", p->max_partitions);
     if (p->page_size != 16 && p->page_size != 64 && p->page_size != 128)
         return fail(PA_ERR_UNSUPPORTED, "page_size %d (supported: 16, 64, 128)", p->page_size);
     if (p->head_dim != 128 && p->head_dim != 256)
@@ -139,11 +142,75 @@ struct Plan {
     pa_plan_info info{};
 };
 
+// Task sizes (tiles) of every (sequence, KV head) when each sequence is cut
+// into partitions of about `tpt` tiles (at most max_parts, at least one).
+static void partition_counts(const std::vector<int>& tiles, int tpt, int max_parts, std::vector<int>* parts) {
+    parts->resize(tiles.size());
+    for (size_t b = 0; b < tiles.size(); ++b)
+        (*parts)[b] = std::max(1, std::min(max_parts, (tiles[b] + tpt - 1) / tpt));
+}
+
+// Estimated completion time (seconds) of a task set launched longest first on
+// `slots` workgroup slots. Running workgroups share the memory system: each
+// streams at min(kWgBytesPerS, kHbmBytesPerS / running). A task costs its KV
+// bytes plus a fixed start/epilogue time; any split sequence adds the merge
+// launch.
+static double plan_cost(const std::vector<int>& tiles, const std::vector<int>& parts, int H, int slots,
+                        double tile_bytes, double partial_bytes, long* ntasks_out) {
+    const double kHbmBytesPerS = 6.0e12;  // sustained HBM read rate of the tile kernel
+    const double kWgBytesPerS = 1.5e10;   // what one workgroup streams on its own (measured 8-18 GB/s)
+    const double kTaskS = 1.0e-6;         // start + four-wave merge + store of one task
+    const double kMergeS = 4.0e-6;        // merge kernel launch and tail
+    std::vector<double> bytes;
+    bool split = false;
+    double merge_bytes = 0.0;
+    for (size_t b = 0; b < tiles.size(); ++b) {
+        const int P = parts[b];
+        split |= P > 1;
+        const double pb = P > 1 ? partial_bytes : 0.0;  // written by the task, read by the merge
+        merge_bytes += pb * P * H;
+        for (int q = 0; q < P; ++q) {
+            const long sz = (long)(q + 1) * tiles[b] / P - (long)q * tiles[b] / P;
+            for (int h = 0; h < H; ++h) bytes.push_back(sz * tile_bytes + pb + kTaskS * kWgBytesPerS);
+        }
+    }
+    *ntasks_out = (long)bytes.size();
+    std::sort(bytes.begin(), bytes.end(), std::greater<double>());
+    // processor sharing: every running task advances at the same rate, so the
+    // next to finish is the one with the least bytes left
+    std::priority_queue<double, std::vector<double>, std::greater<double>> run;
+    size_t next = 0;
+    double consumed = 0.0, t = 0.0;
+    while (next < bytes.size() && (int)run.size() < slots) run.push(bytes[next++]);
+    while (!run.empty()) {
+        const double rate = std::min(kWgBytesPerS, kHbmBytesPerS / (double)run.size());
+        const double x = run.top() - consumed;
+        t += x / rate;
+        consumed = run.top();
+        run.pop();
+        if (next < bytes.size()) run.push(consumed + bytes[next++]);
+    }
+    return t + (split ? kMergeS + merge_bytes / kHbmBytesPerS : 0.0);
+}
+
+// KV bytes of one 256-token tile of one KV head.
+static double tile_bytes_of(const pa_problem& p) {
+    const double D = p.head_dim;
+    double per_token;
+    if (p.kv_dtype == PA_KV_BF16)
+        per_token = 4 * D;
+    else if (p.kv_dtype == PA_KV_FP8_E4M3)
+        per_token = 2 * D + (p.scale_mode == PA_SCALE_PER_TOKEN ? 8 : 0);
+    else
+        per_token = 2 * (D / 2 + D / 32);
+    return per_token * pa::kTileTokens;
+}
+
 // Cut every (sequence, KV head) into partitions of contiguous tiles.
-pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, Plan* out) {
+pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int blocks_per_cu, Plan* out) {
     const int B = p.num_seqs, H = p.num_kv_heads;
-    const int max_parts = p.max_partitions > 0 ? std::min(p.max_partitions, 65535) : 64;
-    const int budget = p.task_budget > 0 ? p.task_budget : std::max(1, 2 * num_cus);
+    const int max_parts = p.max_partitions > 0 ? p.max_partitions : 64;
+    const int slots = std::max(1, num_cus * std::max(1, blocks_per_cu));
     const long cap_tokens = (long)p.max_blocks_per_seq * p.page_size;
     std::vector<int> tiles(B);
     for (int b = 0; b < B; ++b) {
@@ -162,13 +229,42 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, Plan
         tiles[b] = (int)((L + pa::kTileTokens - 1) / pa::kTileTokens);
     }
     long work = 0;
-    for (int b = 0; b < B; ++b) work += (long)tiles[b] * H;
-    const int tpt = (int)std::max<long>(1, (work + budget - 1) / budget);  // target tiles per task
+    int tmax = 0;
+    for (int b = 0; b < B; ++b) {
+        work += (long)tiles[b] * H;
+        tmax = std::max(tmax, tiles[b]);
+    }
+    int tpt;
+    std::vector<int> parts;
+    if (p.task_budget > 0) {
+        tpt = (int)std::max<long>(1, (work + p.task_budget - 1) / p.task_budget);
+        partition_counts(tiles, tpt, max_parts, &parts);
+    } else {
+        // pick the tiles-per-task target with the lowest estimated completion time
+        tpt = std::max(1, tmax);
+        partition_counts(tiles, tpt, max_parts, &parts);
+        long nt = 0;
+        const double tb = tile_bytes_of(p);
+        const double pbytes = (double)rows_of(p) * (p.head_dim + 2) * 4.0;  // one task's partial (O, m, l)
+        double best = plan_cost(tiles, parts, H, slots, tb, pbytes, &nt);
+        std::vector<int> cand;
+        for (int t = tmax - 1; t >= 1; --t) {
+            partition_counts(tiles, t, max_parts, &cand);
+            if (cand == parts) continue;
+            double c = plan_cost(tiles, cand, H, slots, tb, pbytes, &nt);
+            if (nt > 8L * slots) break;
+            if (c < best * 0.995) {
+                best = c;
+                tpt = t;
+                parts = cand;
+            }
+        }
+    }
     out->tasks.clear();
     out->seq_parts.assign(2 * (size_t)B, 0);
     int slot = 0, maxp = 0;
     for (int b = 0; b < B; ++b) {
-        int P = std::max(1, std::min(max_parts, (tiles[b] + tpt - 1) / tpt));
+        const int P = parts[b];
         maxp = std::max(maxp, P);
         out->seq_parts[2 * b] = P;
         out->seq_parts[2 * b + 1] = P > 1 ? slot : -1;
@@ -197,6 +293,7 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, Plan
     out->info.tiles_per_task = tpt;
     out->info.merge_needed = slot > 0 ? 1 : 0;
     out->info.num_cus = num_cus;
+    out->info.slots = slots;
     return PA_OK;
 }
 
@@ -226,13 +323,13 @@ const char* pa_last_error(void) { return g_err.c_str(); }
 const char* pa_version(void) { return "pa_decode gfx950 0.1"; }
 
 pa_status pa_plan_host(const pa_problem* problem, const int32_t* host_context_lens, int32_t num_cus,
-                       int32_t* tasks_out, int32_t task_capacity, int32_t* num_tasks, int32_t* seq_parts_out,
-                       pa_plan_info* info) {
+                       int32_t blocks_per_cu, int32_t* tasks_out, int32_t task_capacity, int32_t* num_tasks,
+                       int32_t* seq_parts_out, pa_plan_info* info) {
     pa_status st = validate(problem);
     if (st != PA_OK) return st;
-    if (num_cus < 1) return fail(PA_ERR_INVALID_ARG, "num_cus must be >= 1");
+    if (num_cus < 1 || blocks_per_cu < 1) return fail(PA_ERR_INVALID_ARG, "num_cus and blocks_per_cu must be >= 1");
     Plan plan;
-    st = build_plan(*problem, host_context_lens, num_cus, &plan);
+    st = build_plan(*problem, host_context_lens, num_cus, blocks_per_cu, &plan);
     if (st != PA_OK) return st;
     if (num_tasks) *num_tasks = plan.info.num_tasks;
     if (info) *info = plan.info;
@@ -257,7 +354,7 @@ pa_status pa_plan(const pa_problem* problem, const int32_t* host_context_lens, p
     const pa::KernelKey key = key_of(*problem);
     if (!pa::have_tile_kernel(key)) return fail(PA_ERR_UNSUPPORTED, "no kernel instance for this problem");
     Plan plan;
-    st = build_plan(*problem, host_context_lens, dev.num_cus, &plan);
+    st = build_plan(*problem, host_context_lens, dev.num_cus, pa::tile_blocks_per_cu(key), &plan);
     if (st != PA_OK) return st;
 
     pa_plan_t* p = new (std::nothrow) pa_plan_t();
@@ -298,8 +395,9 @@ pa_status pa_plan(const pa_problem* problem, const int32_t* host_context_lens, p
         return fail(PA_ERR_HIP, "plan upload sync failed: %s", hipGetErrorString(e));
     }
     if (std::getenv("PA_LOG"))
-        std::fprintf(stderr, "[pa] plan: %d tasks, %d tiles/task target, max %d partitions, %d partial slots, %zu B workspace\n",
-                     plan.info.num_tasks, plan.info.tiles_per_task, plan.info.max_parts, plan.info.total_parts, p->ws_bytes);
+        std::fprintf(stderr, "[pa] plan: %d tasks on %d slots, %d tiles/task target, max %d partitions, %d partial slots, %zu B workspace\n",
+                     plan.info.num_tasks, plan.info.slots, plan.info.tiles_per_task, plan.info.max_parts,
+                     plan.info.total_parts, p->ws_bytes);
     *plan_out = p;
     return PA_OK;
 }

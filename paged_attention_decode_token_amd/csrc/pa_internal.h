@@ -48,4 +48,7 @@ hipError_t launch_merge(const TileArgs& args, int head_dim, hipStream_t stream);
 // Whether an instance exists for `key`.
 bool have_tile_kernel(const KernelKey& key);
 
+// Tile-kernel workgroups of `key` that fit on one compute unit at once.
+int tile_blocks_per_cu(const KernelKey& key);
+
 }  // namespace pa

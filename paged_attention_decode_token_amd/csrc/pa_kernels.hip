@@ -310,46 +310,107 @@ PA_DEV int page_of(const TileArgs& a, const Ctx& cx, int slot) {
     return p;
 }
 
-// One 64-token slice [cb, cb + 64) of one wave.
-template <class C, bool MASK>
-PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>& st, int cb, char* vlds) {
-    constexpr int D = C::D, PG = C::PG, NT = C::NT;
-    const int ln = cx.ln, lg = cx.lg, lane = cx.lane;
+// ------------------------------------------------------ per-slice stages
+//
+// A wave processes the 64-token slice [cb, cb + 64) of every tile of its task.
+// The work is split into load stages (addresses + global loads into
+// registers) and compute stages, so that the loads of slice i + 1 are in
+// flight while slice i computes: K(i + 1) is issued after QK(i), V(i + 1)
+// after PV(i). Loads never depend on whether a slice is the boundary slice;
+// page slots past the owned pages read block 0 and the compute stages mask.
 
-    // ---- pages of this slice. pg[q] (uniform) is only ever indexed with
-    // compile-time q; lanes whose page depends on the lane read the table.
-    int pg[C::NPC];
+template <class C>
+struct SlicePages {
+    int pg[C::NPC];  // uniform page ids of the slice (compile-time indexed only)
+    int kpage;       // page of this lane's K rows
+    int tpage;       // page of this lane's 16 score / transposed-V tokens
+    int cb;
+};
+
+template <class C>
+struct KBuf {
+    u32x4 k[4][C::KLOADS];  // call c: token 16*(ln>>2) + 4c + (ln&3), bytes 64u + 16*lg
+    uint32_t ksc[4];        // MXFP4: e8m0 byte of block lg of those tokens
+    float tks[16], tvs[16]; // per-token scales of tokens 16*lg + [0, 16)
+};
+
+template <class C>
+struct VBuf {
+    u32x4 v[C::STAGE_V ? 2 : 1][C::STAGE_V ? C::IPS : 1];  // token-major rows to stage
+    uint32_t vsc[C::STAGE_V ? 2 : 1][C::STAGE_V ? C::IPS : 1];
+    u32x4 vt[C::VT ? C::DT : 1][C::VT ? (C::ESZ == 2 ? 2 : 1) : 1];  // transposed V
+};
+
+template <class C>
+struct PFrag {
+    u32x4 hi[2][C::NT];  // P^T B operand of PV steps 0 / 1 (bf16)
+    u32x4 lo[2][C::NT];  // low parts when PSPLIT
+};
+
+// slot inside its page of slice token t (t in [0, 64))
+template <class C>
+PA_DEV int slot_in_page(const SlicePages<C>& sp, int t) {
+    if constexpr (C::NPC == 1) return (C::PG > 64 ? (sp.cb % C::PG) : 0) + t;
+    return t & (C::PG - 1);
+}
+
+// Page ids of upcoming slices, prefetched one VGPR at a time so the KV loads
+// of a slice never wait on a block-table read: lane l holds the page of slot q
+// = l % NPC of the wave's slice in tile `tile0 + l / NPC` (block 0 past the
+// owned pages, clamped into the pool).
+template <class C>
+struct PageCache {
+    static constexpr int SPAN = 64 / C::NPC;  // slices covered by one load
+    int tile0;
+    int pgv;
+};
+
+template <class C>
+PA_DEV void page_cache_fill(const TileArgs& a, const Ctx& cx, PageCache<C>& pc, int tile0) {
+    pc.tile0 = tile0;
+    const int tile = tile0 + cx.lane / C::NPC;
+    const int slot = (tile * kTileTokens + 64 * cx.wave) / C::PG + cx.lane % C::NPC;
+    pc.pgv = page_of<true>(a, cx, slot);
+}
+
+PA_DEV int lane_value(int v, int src_lane) { return __builtin_amdgcn_ds_bpermute(src_lane << 2, v); }
+
+template <class C>
+PA_DEV SlicePages<C> slice_pages(const TileArgs& a, const Ctx& cx, PageCache<C>& pc, int tile) {
+    if (tile - pc.tile0 >= PageCache<C>::SPAN) page_cache_fill(a, cx, pc, tile);
+    const int base = (tile - pc.tile0) * C::NPC;
+    SlicePages<C> sp;
+    sp.cb = tile * kTileTokens + 64 * cx.wave;
 #pragma unroll
-    for (int q = 0; q < C::NPC; ++q) pg[q] = uniform(page_of<MASK>(a, cx, cb / PG + q));
-    const int inoff = (PG > 64) ? (cb % PG) : 0;  // slice offset inside its page (PG = 128)
-    // slot inside its page of slice token t (t in [0, 64))
-    auto slot_of = [&](int t) -> int { return C::NPC == 1 ? inoff + t : (t & (PG - 1)); };
-    // page of a per-lane slice token t
-    auto lane_page = [&](int t) -> int { return C::NPC == 1 ? pg[0] : page_of<MASK>(a, cx, cb / PG + t / PG); };
+    for (int q = 0; q < C::NPC; ++q) sp.pg[q] = __builtin_amdgcn_readlane(pc.pgv, base + q);
+    if constexpr (C::NPC == 1) {
+        sp.kpage = sp.tpage = sp.pg[0];
+    } else {
+        sp.kpage = lane_value(pc.pgv, base + (cx.ln >> 2));  // token 16*(ln>>2) + ..
+        sp.tpage = lane_value(pc.pgv, base + cx.lg);         // token 16*lg + ..
+    }
+    return sp;
+}
 
-    // ---- K loads: lane (m = ln, g = lg), call c holds token 16*(ln>>2) + 4c + (ln&3)
+template <class C>
+PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KBuf<C>& kb) {
+    constexpr int PG = C::PG;
+    const int ln = cx.ln, lg = cx.lg;
     const int ktok0 = 16 * (ln >> 2) + (ln & 3);
-    const int kpage = lane_page(ktok0);
-    const char* krow = cx.kbase + (long)kpage * a.num_kv_heads * C::PAGE_BYTES_HEAD +
-                       (long)slot_of(ktok0) * C::ROWB;
-    u32x4 kr[4][C::KLOADS];
+    const char* krow = cx.kbase + (long)sp.kpage * a.num_kv_heads * C::PAGE_BYTES_HEAD +
+                       (long)slot_in_page(sp, ktok0) * C::ROWB;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int u = 0; u < C::KLOADS; ++u) kr[c][u] = ld16(krow + 4 * c * C::ROWB + 64 * u + 16 * lg);
-    uint32_t ksc[4];
+        for (int u = 0; u < C::KLOADS; ++u) kb.k[c][u] = ld16(krow + 4 * c * C::ROWB + 64 * u + 16 * lg);
     if constexpr (C::KV == KV_MXFP4) {
-        const char* srow = cx.ksbase + (long)kpage * a.num_kv_heads * PG * C::SROWB +
-                           (long)slot_of(ktok0) * C::SROWB;
+        const char* srow = cx.ksbase + (long)sp.kpage * a.num_kv_heads * PG * C::SROWB +
+                           (long)slot_in_page(sp, ktok0) * C::SROWB;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ksc[c] = (ld4(srow + 4 * c * C::SROWB) >> (8 * lg)) & 0xFFu;
+        for (int c = 0; c < 4; ++c) kb.ksc[c] = (ld4(srow + 4 * c * C::SROWB) >> (8 * lg)) & 0xFFu;
     }
-
-    // ---- per-token scales of this lane's score/P tokens 16*lg + [0, 16)
-    float tks[16], tvs[16];
     if constexpr (C::SC == SC_TOKEN) {
-        const int t0 = 16 * lg;
-        const long off = ((long)lane_page(t0) * a.num_kv_heads * PG + slot_of(t0)) * 4;
+        const long off = ((long)sp.tpage * a.num_kv_heads * PG + slot_in_page(sp, 16 * lg)) * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             u32x4 kv4 = ld16(cx.ksbase + off + 16 * i), vv4 = ld16(cx.vsbase + off + 16 * i);
@@ -358,26 +419,20 @@ PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>
                 // element first, then reinterpret: bit-casting a vector
                 // element expression directly yields element 0 with this clang
                 const uint32_t kw = kv4[j], vw = vv4[j];
-                tks[4 * i + j] = __builtin_bit_cast(float, kw);
-                tvs[4 * i + j] = __builtin_bit_cast(float, vw);
-            }
-        }
-        if (MASK) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const bool ok = cb + t0 + i < cx.L;
-                tks[i] = ok ? tks[i] : 0.f;
-                tvs[i] = ok ? tvs[i] : 0.f;
+                kb.tks[4 * i + j] = __builtin_bit_cast(float, kw);
+                kb.tvs[4 * i + j] = __builtin_bit_cast(float, vw);
             }
         }
     }
+}
 
-    // ---- V loads
-    // token-major: step s stages slice tokens 16*(e>>3) + 8s + (e&7), e in [0, 32)
-    u32x4 vr[2][C::IPS];
-    uint32_t vsc[2][C::IPS];
-    const int vseg = lane % C::LPR;
+template <class C>
+PA_DEV void load_v(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, VBuf<C>& vb) {
+    constexpr int PG = C::PG;
+    const int ln = cx.ln, lg = cx.lg, lane = cx.lane;
     if constexpr (C::STAGE_V) {
+        // step s stages slice tokens 16*(e>>3) + 8s + (e&7), e in [0, 32)
+        const int vseg = lane % C::LPR;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -385,39 +440,31 @@ PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>
                 const int e = i * C::TPI + lane / C::LPR;
                 const int t = 16 * (e >> 3) + 8 * s + (e & 7);
                 // page of token t: e >> 3 is the same for every lane of instruction i
-                const int vpage = pg[C::NPC == 1 ? 0 : ((i * C::TPI) >> 3) * 16 / PG];
-                const long row = (long)vpage * a.num_kv_heads * PG + slot_of(t);
-                vr[s][i] = ld16(cx.vbase + row * C::ROWB + 16 * vseg);
-                if constexpr (C::KV == KV_MXFP4) vsc[s][i] = (ld4(cx.vsbase + row * C::SROWB) >> (8 * vseg)) & 0xFFu;
+                const int vpage = sp.pg[C::NPC == 1 ? 0 : ((i * C::TPI) >> 3) * 16 / PG];
+                const long row = (long)vpage * a.num_kv_heads * PG + slot_in_page(sp, t);
+                vb.v[s][i] = ld16(cx.vbase + row * C::ROWB + 16 * vseg);
+                if constexpr (C::KV == KV_MXFP4) vb.vsc[s][i] = (ld4(cx.vsbase + row * C::SROWB) >> (8 * vseg)) & 0xFFu;
             }
     }
-    // transposed: lane (d = 16dt + ln, lg) holds slice tokens 16*lg + [0, 16) of row d
-    constexpr int VTW = C::VT ? (C::ESZ == 2 ? 2 : 1) : 0;  // 16-byte loads per d tile
-    u32x4 vt[C::VT ? C::DT : 1][VTW > 0 ? VTW : 1];
     if constexpr (C::VT) {
-        const int t0 = 16 * lg;
-        const char* vcol = cx.vbase + (long)lane_page(t0) * a.num_kv_heads * C::PAGE_BYTES_HEAD +
-                           (long)slot_of(t0) * C::ESZ;
+        // lane (d = 16dt + ln, lg) holds slice tokens 16*lg + [0, 16) of row d
+        constexpr int VTW = C::ESZ == 2 ? 2 : 1;
+        const char* vcol = cx.vbase + (long)sp.tpage * a.num_kv_heads * C::PAGE_BYTES_HEAD +
+                           (long)slot_in_page(sp, 16 * lg) * C::ESZ;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-            for (int w = 0; w < VTW; ++w) vt[dt][w] = ld16(vcol + (long)(16 * dt + ln) * PG * C::ESZ + 16 * w);
-        if (MASK) {
-            // keep only the bytes of tokens < L (byte-granular, PR #7092 "Fix")
-            const int valid = cx.L - (cb + t0);  // tokens of this lane's 16 that are owned
-#pragma unroll
-            for (int w = 0; w < VTW; ++w)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int first = (16 * w + 4 * j) / C::ESZ;  // first token of this dword
-                    uint32_t mk = keep_bytes((valid - first) * C::ESZ);
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt) vt[dt][w][j] &= mk;
-                }
-        }
+            for (int w = 0; w < VTW; ++w) vb.vt[dt][w] = ld16(vcol + (long)(16 * dt + ln) * PG * C::ESZ + 16 * w);
     }
+}
 
-    // ---- QK: S^T[token][row]; acc[c][nt][j] <-> slice token 16*lg + 4c + j, row 16nt + ln
+// QK, scale, mask, online softmax (base 2) -> P^T fragments.
+template <class C, bool MASK>
+PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, const KBuf<C>& kb, State<C>& st,
+                       PFrag<C>& pf, int cb) {
+    constexpr int NT = C::NT;
+    const int lg = cx.lg;
+    // S^T[token][row]; acc[c][nt][j] <-> slice token 16*lg + 4c + j, row 16nt + ln
     f32x4 acc[4][NT];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -425,32 +472,37 @@ PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
             if constexpr (C::MXS) {
-                i32x8 ka = {(int)kr[c][0][0], (int)kr[c][0][1], (int)kr[c][0][2], (int)kr[c][0][3], 0, 0, 0, 0};
-                s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf.q8[nt], s, 4, 0, 0, (int)ksc[c], 0,
+                i32x8 ka = {(int)kb.k[c][0][0], (int)kb.k[c][0][1], (int)kb.k[c][0][2], (int)kb.k[c][0][3], 0, 0, 0, 0};
+                s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf.q8[nt], s, 4, 0, 0, (int)kb.ksc[c], 0,
                                                                      qf.qsc[nt]);
             } else if constexpr (C::KV == KV_MXFP4) {
                 // K widened exactly: dword st holds d = 32g + 8st + [0, 8) times its block scale
-                const float ksf = e8m0_to_f32(ksc[c]);
+                const float ksf = e8m0_to_f32(kb.ksc[c]);
 #pragma unroll
                 for (int st = 0; st < C::KSTEPS; ++st)
-                    s = mfma_bf16(as_bf16x8(fp4x8_to_bf16x8(kr[c][0][st], ksf)), qf.q[nt][st], s);
+                    s = mfma_bf16(as_bf16x8(fp4x8_to_bf16x8(kb.k[c][0][st], ksf)), qf.q[nt][st], s);
             } else if constexpr (C::KV == KV_BF16) {
 #pragma unroll
-                for (int ks = 0; ks < C::KSTEPS; ++ks) s = mfma_bf16(as_bf16x8(kr[c][ks]), qf.q[nt][ks], s);
+                for (int ks = 0; ks < C::KSTEPS; ++ks) s = mfma_bf16(as_bf16x8(kb.k[c][ks]), qf.q[nt][ks], s);
             } else {
 #pragma unroll
                 for (int u = 0; u < C::KLOADS; ++u) {
-                    s = mfma_bf16(fp8x8_to_bf16x8(kr[c][u][0], kr[c][u][1]), qf.q[nt][2 * u], s);
-                    s = mfma_bf16(fp8x8_to_bf16x8(kr[c][u][2], kr[c][u][3]), qf.q[nt][2 * u + 1], s);
+                    s = mfma_bf16(fp8x8_to_bf16x8(kb.k[c][u][0], kb.k[c][u][1]), qf.q[nt][2 * u], s);
+                    s = mfma_bf16(fp8x8_to_bf16x8(kb.k[c][u][2], kb.k[c][u][3]), qf.q[nt][2 * u + 1], s);
                 }
             }
             acc[c][nt] = s;
         }
 
-    // ---- scale, mask, online softmax (base 2), P^T fragments
     const float sc = a.scale_log2 * cx.kscale;
-    u32x4 pf[2][NT];   // P^T B-operand for PV steps 0/1
-    u32x4 pfl[2][NT];  // low parts of P when PSPLIT
+    float tvs[16];
+    if constexpr (C::SC == SC_TOKEN) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            // per-token V scales of tokens at or past L are staged as 0 (PR #7092, "Fix")
+            tvs[i] = (!MASK || cb + 16 * lg + i < cx.L) ? kb.tvs[i] : 0.f;
+        }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         float mloc = -__builtin_inff();
@@ -460,8 +512,8 @@ PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * lg + 4 * c + j;
                 float x = acc[c][nt][j] * sc;
-                if constexpr (C::SC == SC_TOKEN) x *= tks[4 * c + j];
-                if (MASK) x = (cb + t < cx.L) ? x : -__builtin_inff();
+                if constexpr (C::SC == SC_TOKEN) x *= kb.tks[4 * c + j];
+                if (MASK) x = (cb + t < cx.L) ? x : -__builtin_inff();  // select, never a multiply
                 acc[c][nt][j] = x;
                 mloc = fmaxf(mloc, x);
             }
@@ -495,28 +547,62 @@ PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>
         }
         st.l[nt] = st.l[nt] * alpha + lsum;
         // step s uses calls 2s (tokens 16lg + 8s + 0..3) and 2s + 1 (16lg + 8s + 4..7)
-        pf[0][nt] = u32x4{pw[0], pw[1], pw[2], pw[3]};
-        pf[1][nt] = u32x4{pw[4], pw[5], pw[6], pw[7]};
+        pf.hi[0][nt] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+        pf.hi[1][nt] = u32x4{pw[4], pw[5], pw[6], pw[7]};
         if constexpr (C::PSPLIT) {
-            pfl[0][nt] = u32x4{plo[0], plo[1], plo[2], plo[3]};
-            pfl[1][nt] = u32x4{plo[4], plo[5], plo[6], plo[7]};
+            pf.lo[0][nt] = u32x4{plo[0], plo[1], plo[2], plo[3]};
+            pf.lo[1][nt] = u32x4{plo[4], plo[5], plo[6], plo[7]};
         }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] *= alpha;
     }
+}
 
-    // ---- PV
+PA_DEV void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// V operand preparation (boundary mask) and O^T[d][row] += V^T . P^T.
+template <class C, bool MASK>
+PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& st, int cb, char* vlds) {
+    constexpr int NT = C::NT;
+    const int ln = cx.ln, lg = cx.lg, lane = cx.lane;
+    u32x4 vt[C::VT ? C::DT : 1][C::VT ? (C::ESZ == 2 ? 2 : 1) : 1];
+    if constexpr (C::VT) {
+        constexpr int VTW = C::ESZ == 2 ? 2 : 1;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int w = 0; w < VTW; ++w) vt[dt][w] = vb.vt[dt][w];
+        if (MASK) {
+            // keep only the bytes of tokens < L (byte-granular, PR #7092 "Fix")
+            const int valid = cx.L - (cb + 16 * lg);  // owned tokens among this lane's 16
+#pragma unroll
+            for (int w = 0; w < VTW; ++w)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int first = (16 * w + 4 * j) / C::ESZ;  // first token of this dword
+                    const uint32_t mk = keep_bytes((valid - first) * C::ESZ);
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) vt[dt][w][j] &= mk;
+                }
+        }
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         if constexpr (C::STAGE_V) {
-            // stage rows e of step s into the wave's LDS tile (bf16, row pitch VPITCH)
+            // stage rows e of step s into the wave's LDS tile (bf16, row pitch VPITCH);
+            // rows of tokens at or past L are written as zeros
+            const int vseg = lane % C::LPR;
 #pragma unroll
             for (int i = 0; i < C::IPS; ++i) {
                 const int e = i * C::TPI + lane / C::LPR;
                 const int t = 16 * (e >> 3) + 8 * s + (e & 7);
                 const bool ok = !MASK || (cb + t < cx.L);
                 char* dst = vlds + e * C::VPITCH;
-                u32x4 raw = vr[s][i];
+                u32x4 raw = vb.v[s][i];
                 if constexpr (C::KV == KV_BF16) {
                     if (!ok) raw = u32x4{0, 0, 0, 0};
                     *reinterpret_cast<u32x4*>(dst + 16 * vseg) = raw;
@@ -527,7 +613,7 @@ PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>
                     *reinterpret_cast<u32x4*>(dst + 32 * vseg) = u32x4{a0[0], a0[1], a1[0], a1[1]};
                     *reinterpret_cast<u32x4*>(dst + 32 * vseg + 16) = u32x4{a2[0], a2[1], a3[0], a3[1]};
                 } else {
-                    const float vsf = e8m0_to_f32(vsc[s][i]);
+                    const float vsf = e8m0_to_f32(vb.vsc[s][i]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         u32x4 w = fp4x8_to_bf16x8(raw[j], vsf);
@@ -536,10 +622,7 @@ PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>
                     }
                 }
             }
-            // staged rows are read back by other lanes of the same wave
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            wave_lds_sync();  // staged rows are read back by other lanes of the same wave
         }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
@@ -559,16 +642,11 @@ PA_DEV void slice(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, State<C>
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pf[s][nt]), st.o[dt][nt]);
-                if constexpr (C::PSPLIT) st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pfl[s][nt]), st.o[dt][nt]);
+                st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pf.hi[s][nt]), st.o[dt][nt]);
+                if constexpr (C::PSPLIT) st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pf.lo[s][nt]), st.o[dt][nt]);
             }
         }
-        if constexpr (C::STAGE_V) {
-            // the next step overwrites the tile: all lanes' reads must be done
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        if constexpr (C::STAGE_V) wave_lds_sync();  // the next step overwrites the tile
     }
 }
 
@@ -628,13 +706,39 @@ __global__ __launch_bounds__(kTileThreads) void pa_tile_kernel(const TileArgs a)
     }
 
     char* vlds = smem + cx.wave * C::VSTAGE_BYTES;
-    // full tiles: every token of the tile is owned
-    const int te_full = min(te, L / kTileTokens);
-    for (int tile = tb; tile < te_full; ++tile) slice<C, false>(a, cx, qf, st, tile * kTileTokens + 64 * cx.wave, vlds);
-    // the boundary tile (peeled): masked
-    if (te > te_full && te_full >= tb) {
-        const int cb = te_full * kTileTokens + 64 * cx.wave;
-        if (cb < L) slice<C, true>(a, cx, qf, st, cb, vlds);
+    // Tiles [tb, te_full) are full (every token owned); tile te - 1 is the
+    // peeled boundary tile when te > te_full. Loads run one stage ahead.
+    const int te_full = max(tb, min(te, L / kTileTokens));
+    const int nfull = te_full - tb;
+    const bool has_bnd = te > te_full;
+    const int total = nfull + (has_bnd ? 1 : 0);
+    if (total > 0) {
+        int cb = tb * kTileTokens + 64 * cx.wave;
+        PageCache<C> pc;
+        page_cache_fill<C>(a, cx, pc, tb);
+        SlicePages<C> sp = slice_pages<C>(a, cx, pc, tb);
+        KBuf<C> kb;
+        VBuf<C> vb;
+        load_k<C>(a, cx, sp, kb);
+        load_v<C>(a, cx, sp, vb);
+        for (int j = 0; j < nfull; ++j) {
+            PFrag<C> pf;
+            qk_softmax<C, false>(a, cx, qf, kb, st, pf, cb);
+            const bool more = j + 1 < total;
+            SlicePages<C> spn;
+            if (more) {
+                spn = slice_pages<C>(a, cx, pc, tb + j + 1);
+                load_k<C>(a, cx, spn, kb);
+            }
+            pv<C, false>(cx, vb, pf, st, cb, vlds);
+            if (more) load_v<C>(a, cx, spn, vb);
+            cb += kTileTokens;
+        }
+        if (has_bnd) {
+            PFrag<C> pf;
+            qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb);
+            pv<C, true>(cx, vb, pf, st, cb, vlds);
+        }
     }
 
     // ---- merge the four waves (fixed order), then store
@@ -736,9 +840,22 @@ __global__ __launch_bounds__(kTileThreads) void pa_tile_kernel(const TileArgs a)
 
 // ------------------------------------------------------------- merge kernel
 
+PA_DEV float wave_max(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor(v, m));
+    return v;
+}
+PA_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += shfl_xor(v, m);
+    return v;
+}
+
 // One wave per output row (b, i, h) of a sequence with more than one
-// partition: M = max_p m_p, w_p = 2^(m_p - M), out = sum_p w_p O_p / sum_p w_p l_p
-// in partition order (PR #7056, "Bandwidth": the partition reducer).
+// partition (at most 64): M = max_p m_p, w_p = 2^(m_p - M),
+// out = sum_p w_p O_p / sum_p w_p l_p, summed in partition order (PR #7056,
+// "Bandwidth": the partition reducer). Lane p reads partition p's (m, l); the
+// weighted sum of the O_p rows then runs over p with D/64 elements per lane.
 template <int D>
 __global__ __launch_bounds__(256) void pa_merge_kernel(const TileArgs a) {
     const int lane = threadIdx.x & 63;
@@ -754,29 +871,40 @@ __global__ __launch_bounds__(256) void pa_merge_kernel(const TileArgs a) {
     const int P = a.seq_parts[2 * b];
     if (P <= 1) return;
     const long slot0 = a.seq_parts[2 * b + 1];
+    const long stride = (long)a.num_kv_heads * a.rows;  // rows between consecutive partitions
+    const long prow0 = (slot0 * a.num_kv_heads + kvh) * a.rows + r;
+    float m = -__builtin_inff(), l = 0.f;
+    if (lane < P) {
+        const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * (prow0 + lane * stride));
+        m = ml[0];
+        l = ml[1];
+    }
+    const float M = wave_max(m);
+    const float w = (lane < P && M != -__builtin_inff()) ? fast_exp2(m - M) : 0.f;
+    const float den = wave_sum(w * l);
     constexpr int PER = D / 64;
-    float M = -__builtin_inff();
-    for (int p = 0; p < P; ++p) M = fmaxf(M, a.part_ml[2 * (((slot0 + p) * a.num_kv_heads + kvh) * a.rows + r)]);
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    float den = 0.f;
-    if (M != -__builtin_inff()) {
-        for (int p = 0; p < P; ++p) {
-            const long prow = ((slot0 + p) * a.num_kv_heads + kvh) * a.rows + r;
-            const float w = fast_exp2(a.part_ml[2 * prow] - M);
-            den += w * a.part_ml[2 * prow + 1];
-            const float* po = a.part_o + prow * D + PER * lane;
-            if constexpr (PER == 2) {
-                f32x2 v = *reinterpret_cast<const f32x2*>(po);
-                acc[0] += w * v[0];
-                acc[1] += w * v[1];
-            } else {
-                f32x4 v = *reinterpret_cast<const f32x4*>(po);
+    const float* po = a.part_o + prow0 * D + PER * lane;
+    int p = 0;
+    for (; p + 4 <= P; p += 4) {
+        float v[4][PER];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) acc[k] += w * v[k];
-            }
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < PER; ++k) v[u][k] = po[(p + u) * stride * D + k];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), p + u));
+#pragma unroll
+            for (int k = 0; k < PER; ++k) acc[k] += wp * v[u][k];
         }
+    }
+    for (; p < P; ++p) {
+        const float wp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), p));
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] += wp * po[p * stride * D + k];
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     char* op = reinterpret_cast<char*>(a.out) + R * D * 2 + 2 * PER * lane;
@@ -824,6 +952,14 @@ static TileFn find(const KernelKey& k) {
 }
 
 bool have_tile_kernel(const KernelKey& key) { return find(key) != nullptr; }
+
+int tile_blocks_per_cu(const KernelKey& key) {
+    TileFn fn = find(key);
+    if (!fn) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kTileThreads, 0) != hipSuccess) return 1;
+    return n < 1 ? 1 : n;
+}
 
 hipError_t launch_tile(const KernelKey& key, const TileArgs& args, int num_tasks, hipStream_t stream) {
     TileFn fn = find(key);
