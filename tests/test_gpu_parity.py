@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
-Bar (the survey's reading of the target): rel-L2 = ||gpu - o|| / ||o|| <= 3e-3
+Bar: rel-L2 = ||gpu - o|| / ||o|| <= 3e-3
 over the compared rows, and |gpu_i - o_i| <= 2e-2 * max(1, |o_i|) per element,
 where o is the oracle's unrounded fp64 result and gpu is the bf16 output. Plus
 the NaN contract: output finite and bit-identical between runs whose unowned
