@@ -62,6 +62,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 PA_DEV u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 PA_DEV u32x2 ld8(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
 PA_DEV uint32_t ld4(const char* p) { return *reinterpret_cast<const uint32_t*>(p); }
+// KV cache bytes are read once per call: nontemporal loads keep them from
+// displacing reused data in the caches and stream measurably faster on gfx950.
+// Used only where one wave reads every byte of the 128-byte lines it touches:
+// a transposed V row of a page and the per-token scales of a page are split
+// between waves or heads, and an evict-first line would be fetched twice.
+PA_DEV u32x4 ld16_kv(const char* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+PA_DEV uint32_t ld4_kv(const char* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
 
 PA_DEV int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -402,12 +409,12 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int u = 0; u < C::KLOADS; ++u) kb.k[c][u] = ld16(krow + 4 * c * C::ROWB + 64 * u + 16 * lg);
+        for (int u = 0; u < C::KLOADS; ++u) kb.k[c][u] = ld16_kv(krow + 4 * c * C::ROWB + 64 * u + 16 * lg);
     if constexpr (C::KV == KV_MXFP4) {
         const char* srow = cx.ksbase + (long)sp.kpage * a.num_kv_heads * PG * C::SROWB +
                            (long)slot_in_page(sp, ktok0) * C::SROWB;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kb.ksc[c] = (ld4(srow + 4 * c * C::SROWB) >> (8 * lg)) & 0xFFu;
+        for (int c = 0; c < 4; ++c) kb.ksc[c] = (ld4_kv(srow + 4 * c * C::SROWB) >> (8 * lg)) & 0xFFu;
     }
     if constexpr (C::SC == SC_TOKEN) {
         const long off = ((long)sp.tpage * a.num_kv_heads * PG + slot_in_page(sp, 16 * lg)) * 4;
@@ -442,8 +449,8 @@ PA_DEV void load_v(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, VB
                 // page of token t: e >> 3 is the same for every lane of instruction i
                 const int vpage = sp.pg[C::NPC == 1 ? 0 : ((i * C::TPI) >> 3) * 16 / PG];
                 const long row = (long)vpage * a.num_kv_heads * PG + slot_in_page(sp, t);
-                vb.v[s][i] = ld16(cx.vbase + row * C::ROWB + 16 * vseg);
-                if constexpr (C::KV == KV_MXFP4) vb.vsc[s][i] = (ld4(cx.vsbase + row * C::SROWB) >> (8 * vseg)) & 0xFFu;
+                vb.v[s][i] = ld16_kv(cx.vbase + row * C::ROWB + 16 * vseg);
+                if constexpr (C::KV == KV_MXFP4) vb.vsc[s][i] = (ld4_kv(cx.vsbase + row * C::SROWB) >> (8 * vseg)) & 0xFFu;
             }
     }
     if constexpr (C::VT) {
