@@ -311,8 +311,12 @@ PA_DEV void load_q(const TileArgs& a, const Ctx& cx, QFrag<C>& qf) {
 // clamped into the pool).
 template <bool MASK>
 PA_DEV int page_of(const TileArgs& a, const Ctx& cx, int slot) {
-    int p = 0;
-    if (!MASK || slot < cx.npages) p = cx.bt_row[slot];
+    // The read is unconditional, since a per-lane branch here would make every
+    // loop that refills page ids divergent. Past the owned pages it re-reads
+    // the last owned column, and the select pins the slot to block 0.
+    const int col = MASK ? min(slot, max(cx.npages - 1, 0)) : slot;
+    int p = cx.bt_row[col];
+    if (MASK && slot >= cx.npages) p = 0;
     p = p < 0 ? 0 : (p >= a.num_blocks ? a.num_blocks - 1 : p);
     return p;
 }
@@ -337,7 +341,7 @@ struct SlicePages {
 template <class C>
 struct KBuf {
     u32x4 k[4][C::KLOADS];  // call c: token 16*(ln>>2) + 4c + (ln&3), bytes 64u + 16*lg
-    uint32_t ksc[4];        // MXFP4: e8m0 byte of block lg of those tokens
+    uint32_t ksc[4];        // MXFP4: the 4 e8m0 bytes of those tokens (byte lg is this lane's block)
     float tks[16], tvs[16]; // per-token scales of tokens 16*lg + [0, 16)
 };
 
@@ -414,7 +418,7 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
         const char* srow = cx.ksbase + (long)sp.kpage * a.num_kv_heads * PG * C::SROWB +
                            (long)slot_in_page(sp, ktok0) * C::SROWB;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kb.ksc[c] = (ld4_kv(srow + 4 * c * C::SROWB) >> (8 * lg)) & 0xFFu;
+        for (int c = 0; c < 4; ++c) kb.ksc[c] = ld4_kv(srow + 4 * c * C::SROWB);  // byte lg is used
     }
     if constexpr (C::SC == SC_TOKEN) {
         const long off = ((long)sp.tpage * a.num_kv_heads * PG + slot_in_page(sp, 16 * lg)) * 4;
@@ -450,7 +454,7 @@ PA_DEV void load_v(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, VB
                 const int vpage = sp.pg[C::NPC == 1 ? 0 : ((i * C::TPI) >> 3) * 16 / PG];
                 const long row = (long)vpage * a.num_kv_heads * PG + slot_in_page(sp, t);
                 vb.v[s][i] = ld16_kv(cx.vbase + row * C::ROWB + 16 * vseg);
-                if constexpr (C::KV == KV_MXFP4) vb.vsc[s][i] = (ld4_kv(cx.vsbase + row * C::SROWB) >> (8 * vseg)) & 0xFFu;
+                if constexpr (C::KV == KV_MXFP4) vb.vsc[s][i] = ld4_kv(cx.vsbase + row * C::SROWB);  // byte vseg is used
             }
     }
     if constexpr (C::VT) {
@@ -480,11 +484,12 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
             if constexpr (C::MXS) {
                 i32x8 ka = {(int)kb.k[c][0][0], (int)kb.k[c][0][1], (int)kb.k[c][0][2], (int)kb.k[c][0][3], 0, 0, 0, 0};
-                s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf.q8[nt], s, 4, 0, 0, (int)kb.ksc[c], 0,
+                s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf.q8[nt], s, 4, 0, 0,
+                                                                     (int)((kb.ksc[c] >> (8 * lg)) & 0xFFu), 0,
                                                                      qf.qsc[nt]);
             } else if constexpr (C::KV == KV_MXFP4) {
                 // K widened exactly: dword st holds d = 32g + 8st + [0, 8) times its block scale
-                const float ksf = e8m0_to_f32(kb.ksc[c]);
+                const float ksf = e8m0_to_f32((kb.ksc[c] >> (8 * lg)) & 0xFFu);
 #pragma unroll
                 for (int st = 0; st < C::KSTEPS; ++st)
                     s = mfma_bf16(as_bf16x8(fp4x8_to_bf16x8(kb.k[c][0][st], ksf)), qf.q[nt][st], s);
@@ -620,7 +625,7 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
                     *reinterpret_cast<u32x4*>(dst + 32 * vseg) = u32x4{a0[0], a0[1], a1[0], a1[1]};
                     *reinterpret_cast<u32x4*>(dst + 32 * vseg + 16) = u32x4{a2[0], a2[1], a3[0], a3[1]};
                 } else {
-                    const float vsf = e8m0_to_f32(vb.vsc[s][i]);
+                    const float vsf = e8m0_to_f32((vb.vsc[s][i] >> (8 * vseg)) & 0xFFu);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         u32x4 w = fp4x8_to_bf16x8(raw[j], vsf);
@@ -664,7 +669,7 @@ __global__ __launch_bounds__(kTileThreads) void pa_tile_kernel(const TileArgs a)
 
     Ctx cx;
     cx.lane = threadIdx.x & 63;
-    cx.wave = threadIdx.x >> 6;
+    cx.wave = uniform(threadIdx.x >> 6);
     cx.ln = cx.lane & 15;
     cx.lg = cx.lane >> 4;
     const int* task = a.tasks + 4 * blockIdx.x;
@@ -714,7 +719,13 @@ __global__ __launch_bounds__(kTileThreads) void pa_tile_kernel(const TileArgs a)
 
     char* vlds = smem + cx.wave * C::VSTAGE_BYTES;
     // Tiles [tb, te_full) are full (every token owned); tile te - 1 is the
-    // peeled boundary tile when te > te_full. Loads run one stage ahead.
+    // boundary tile when te > te_full. Loads run one stage ahead: V(j) is
+    // issued at the top of iteration j (right after PV(j - 1)), K(j + 1) right
+    // after QK(j). Every load of the loop is unconditional and the loop test
+    // comes after PV, so the waits before QK and PV cover exactly the loads
+    // of the current slice, never the prefetch in flight. The last tile of
+    // the task runs after the loop with its own V loads, masked (a no-op on a
+    // full tile).
     const int te_full = max(tb, min(te, L / kTileTokens));
     const int nfull = te_full - tb;
     const bool has_bnd = te > te_full;
@@ -727,25 +738,19 @@ __global__ __launch_bounds__(kTileThreads) void pa_tile_kernel(const TileArgs a)
         KBuf<C> kb;
         VBuf<C> vb;
         load_k<C>(a, cx, sp, kb);
-        load_v<C>(a, cx, sp, vb);
-        for (int j = 0; j < nfull; ++j) {
+        for (int j = 0; j + 1 < total; ++j) {  // full tiles followed by another tile
+            load_v<C>(a, cx, sp, vb);
             PFrag<C> pf;
             qk_softmax<C, false>(a, cx, qf, kb, st, pf, cb);
-            const bool more = j + 1 < total;
-            SlicePages<C> spn;
-            if (more) {
-                spn = slice_pages<C>(a, cx, pc, tb + j + 1);
-                load_k<C>(a, cx, spn, kb);
-            }
+            sp = slice_pages<C>(a, cx, pc, tb + j + 1);
+            load_k<C>(a, cx, sp, kb);
             pv<C, false>(cx, vb, pf, st, cb, vlds);
-            if (more) load_v<C>(a, cx, spn, vb);
             cb += kTileTokens;
         }
-        if (has_bnd) {
-            PFrag<C> pf;
-            qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb);
-            pv<C, true>(cx, vb, pf, st, cb, vlds);
-        }
+        load_v<C>(a, cx, sp, vb);
+        PFrag<C> pf;
+        qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb);
+        pv<C, true>(cx, vb, pf, st, cb, vlds);
     }
 
     // ---- merge the four waves (fixed order), then store
