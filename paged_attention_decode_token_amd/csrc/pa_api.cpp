@@ -152,13 +152,16 @@ static void partition_counts(const std::vector<int>& tiles, int tpt, int max_par
 
 // Estimated completion time (seconds) of a task set launched longest first on
 // `slots` workgroup slots. Running workgroups share the memory system: each
-// streams at min(kWgBytesPerS, kHbmBytesPerS / running). A task costs its KV
-// bytes plus a fixed start/epilogue time; any split sequence adds the merge
-// launch.
+// streams at min(kWgBytesPerS, kHbmBytesPerS / running), where a workgroup on
+// its own is latency-bound at about one 256-token tile per kTileS (its four
+// waves keep one slice of K or V in flight each; measured 4-6 us per tile on
+// bf16, fp8 and MXFP4 caches alike). A task costs its KV bytes plus a fixed
+// start/epilogue time; any split sequence adds the merge launch.
 static double plan_cost(const std::vector<int>& tiles, const std::vector<int>& parts, int H, int slots,
                         double tile_bytes, double partial_bytes, long* ntasks_out) {
-    const double kHbmBytesPerS = 6.0e12;  // sustained HBM read rate of the tile kernel
-    const double kWgBytesPerS = 1.5e10;   // what one workgroup streams on its own (measured 8-18 GB/s)
+    const double kHbmBytesPerS = 6.5e12;  // sustained HBM read rate of the tile kernel
+    const double kTileS = 5.5e-6;         // one workgroup, one tile, latency-bound
+    const double kWgBytesPerS = tile_bytes / kTileS;
     const double kTaskS = 1.0e-6;         // start + four-wave merge + store of one task
     const double kMergeS = 4.0e-6;        // merge kernel launch and tail
     std::vector<double> bytes;

@@ -62,11 +62,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 PA_DEV u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 PA_DEV u32x2 ld8(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
 PA_DEV uint32_t ld4(const char* p) { return *reinterpret_cast<const uint32_t*>(p); }
-// KV cache bytes are read once per call: nontemporal loads keep them from
-// displacing reused data in the caches and stream measurably faster on gfx950.
-// Used only where one wave reads every byte of the 128-byte lines it touches:
-// a transposed V row of a page and the per-token scales of a page are split
-// between waves or heads, and an evict-first line would be fetched twice.
+// KV cache bytes are read once per call. Nontemporal loads stream faster on
+// gfx950 (about 6.9 against 6.2 TB/s for 16 KB pages read 1 KB per
+// instruction), but only when each instruction covers whole 128-byte lines:
+// where one instruction reads half of a line and a later one (or another
+// wave) the other half, the evict-first line is fetched again and the rate
+// drops below that of ordinary loads (5.6 TB/s for the 16-rows x 64-byte
+// pattern of an MFMA A operand). So they are used for token-major V staging
+// (a lane group reads whole rows) and for MXFP4 K (64-byte rows, four adjacent
+// tokens per instruction), and not for K rows of 128 bytes or more, transposed
+// V rows split between two waves, or per-token scales shared between heads.
 PA_DEV u32x4 ld16_kv(const char* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
 PA_DEV uint32_t ld4_kv(const char* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
 
@@ -184,6 +189,11 @@ struct Cfg {
     static constexpr int LPR = ROWB / 16;         // lanes per token row
     static constexpr int TPI = 64 / LPR;          // tokens per load instruction
     static constexpr int IPS = 32 / TPI;          // load instructions per 32-token step
+    // Workgroups per compute unit the register allocation is held to. The loop
+    // keeps one slice of K or V in flight per wave, so resident waves are what
+    // hides HBM latency; these configurations fit 3 waves per SIMD (<= 168
+    // VGPRs) without spilling the loop.
+    static constexpr int MINB = (KV == KV_FP8 && VT && D == 128 && NT == 1) || KV == KV_MXFP4 ? 3 : 1;
 };
 
 template <class C>
@@ -413,7 +423,10 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int u = 0; u < C::KLOADS; ++u) kb.k[c][u] = ld16_kv(krow + 4 * c * C::ROWB + 64 * u + 16 * lg);
+        for (int u = 0; u < C::KLOADS; ++u) {
+            const char* src = krow + 4 * c * C::ROWB + 64 * u + 16 * lg;
+            kb.k[c][u] = C::ROWB <= 64 ? ld16_kv(src) : ld16(src);
+        }
     if constexpr (C::KV == KV_MXFP4) {
         const char* srow = cx.ksbase + (long)sp.kpage * a.num_kv_heads * PG * C::SROWB +
                            (long)slot_in_page(sp, ktok0) * C::SROWB;
@@ -663,7 +676,7 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
 }
 
 template <class C>
-__global__ __launch_bounds__(kTileThreads) void pa_tile_kernel(const TileArgs a) {
+__global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const TileArgs a) {
     constexpr int D = C::D, NT = C::NT, PG = C::PG;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
 
