@@ -65,6 +65,69 @@ def load_traffic(kernel_tag: str):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
+def kernel_tag_of(spec) -> str:
+    """The tile kernel's template arguments as rocprofv3 prints them."""
+    kv = {"bf16": 0, "fp8": 1, "mxfp4": 2}[spec.kv_dtype]
+    sc = {"none": 0, "tensor": 1, "token": 2}[spec.scale_mode]
+    vt = 1 if spec.v_layout == "trans" else 0
+    nt = 1 if spec.qlen * spec.q_per_kv <= 16 else 2
+    qf = 1 if spec.q_dtype == "fp8" else 0
+    return "Cfg<%d, %d, %d, %d, %d, %d, %d, 0>" % (kv, sc, vt, spec.head_dim, spec.page_size, nt, qf)
+
+
+def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
+    """Turn two rocprofv3 --pmc runs of `bench.py --calibrate-copy` (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch) into HBM bytes per tile launch.
+
+    Each counter is scaled by what it reads for the 1 GiB copy kernel of the same
+    run (torch.neg: 1 GiB read, 1 GiB written). Writes `out_json` keyed to the
+    current kernel source and prints a markdown summary."""
+    import csv
+    from collections import defaultdict
+
+    from paged_attention_decode_token_amd import inputs as I
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def one(vals, key):
+        hits = [v for k, v in vals.items() if key in k]
+        if len(hits) != 1:
+            raise SystemExit("expected one kernel matching %r in the counter CSV, found %d" % (key, len(hits)))
+        return hits[0]
+
+    gib_kib = float(1 << 20)
+    f_copy, w_copy = one(fetch, "neg_kernel"), one(write, "neg_kernel")
+    f_factor, w_factor = gib_kib / (sum(f_copy) / len(f_copy)), gib_kib / (sum(w_copy) / len(w_copy))
+    kernels = {}
+    lines = ["| workload | tile kernel | dispatches | HBM read B/launch | HBM write B/launch | algorithmic B | read / algorithmic |",
+             "|---|---|---|---|---|---|---|"]
+    for spec in (I.BF16_P64, I.BF16_P128):
+        tag = kernel_tag_of(spec)
+        fv, wv = one(fetch, tag), one(write, tag)
+        rd = sum(fv) / len(fv) * 1024 * f_factor
+        wr = sum(wv) / len(wv) * 1024 * w_factor
+        alg = I.make_case(spec).kv_bytes()
+        kernels[spec.name] = {"kernel": tag, "dispatches": len(fv), "hbm_read_bytes_per_launch": round(rd),
+                              "hbm_write_bytes_per_launch": round(wr), "hbm_bytes_per_launch": round(rd + wr),
+                              "algorithmic_bytes": alg}
+        lines.append("| %s | %s | %d | %.4g | %.4g | %.4g | %.4f |" % (spec.name, tag, len(fv), rd, wr, alg, rd / alg))
+    doc = {"kernel_source": kernel_source_hash(), "fetch_factor": round(f_factor, 4),
+           "write_factor": round(w_factor, 4), "kernels": kernels}
+    with open(out_json, "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    print("Calibration (1 GiB torch.neg copy): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f\n" % (f_factor, w_factor))
+    print("\n".join(lines))
+
+
 def time_cpu_oracle(case, target_s=15.0):
     import oracle
 
@@ -154,7 +217,13 @@ def main():
                     help="also time every workload (one pa_decode call each) and print a table to stderr")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter calibration)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of "
+                         "`bench.py --calibrate-copy` into profiles/traffic.json")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], os.path.join(ROOT, "profiles", "traffic.json"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
