@@ -163,7 +163,7 @@ static double plan_cost(const std::vector<int>& tiles, const std::vector<int>& p
     const double kTileS = 5.5e-6;         // one workgroup, one tile, latency-bound
     const double kWgBytesPerS = tile_bytes / kTileS;
     const double kTaskS = 1.0e-6;         // start + four-wave merge + store of one task
-    const double kMergeS = 4.0e-6;        // merge kernel launch and tail
+    const double kMergeS = 8.0e-6;        // merge kernel (about 4.5 us) and the gap between the launches
     std::vector<double> bytes;
     bool split = false;
     double merge_bytes = 0.0;

@@ -73,9 +73,15 @@ PA_DEV uint32_t ld4(const char* p) { return *reinterpret_cast<const uint32_t*>(p
 // tokens per instruction), and not for K rows of 128 bytes or more, transposed
 // V rows split between two waves, or per-token scales shared between heads.
 PA_DEV u32x4 ld16_kv(const char* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+constexpr int kLoadNontemporal = 2;  // cache-policy operand of the LDS DMA load: nt
 PA_DEV uint32_t ld4_kv(const char* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
 
 PA_DEV int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// s_waitcnt immediate that waits until at most n vector-memory instructions
+// are outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
 PA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -177,10 +183,20 @@ struct Cfg {
     static constexpr int DT = D / 16;                                // 16-wide d tiles of O
     static constexpr int NPC = PG >= 64 ? 1 : 64 / PG;               // pages per 64-token slice
     static constexpr long PAGE_BYTES_HEAD = (long)PG * ROWB;         // one (page, head) of K or V data
-    // token-major V staged through LDS, one 32-token PV step at a time, bf16
-    static constexpr bool STAGE_V = !VT;
-    static constexpr int VPITCH = D * 2 + 16;                        // LDS row pitch in bytes
-    static constexpr int VSTAGE_BYTES = STAGE_V ? 32 * VPITCH : 0;   // per wave
+    // Token-major V of a bf16 or e4m3 cache goes straight from HBM into a
+    // wave-private LDS tile (64 token rows, XOR-swizzled 16-byte chunks) by
+    // LDS DMA and is read back transposed; MXFP4 V is widened to bf16 in
+    // registers and staged through LDS one 32-token PV step at a time.
+    // Measured per configuration: one N tile only (with 32 query rows the D 256
+    // kernel spills, and the spill traffic shares the vmcnt the DMA wait
+    // counts on), and not for bf16 pages of 128 tokens (there the register
+    // path at one workgroup per CU beats the DMA path at one or two: 179.5
+    // against 183-209 us on the batch-64 workload).
+    static constexpr bool VDMA = !VT && KV != KV_MXFP4 && NT_ == 1 && !(KV_ == KV_BF16 && PG_ == 128);
+    static constexpr bool STAGE_V = !VT && !VDMA;
+    static constexpr int VPITCH = D * 2 + 16;                        // staged bf16 row pitch in bytes
+    static constexpr int CPR = ROWB / 16;                            // 16-byte chunks per V row (DMA)
+    static constexpr int VSTAGE_BYTES = VDMA ? 64 * ROWB : (STAGE_V ? 32 * VPITCH : 0);  // per wave
     static constexpr int ROWS_PAD = 16 * NT;
     static constexpr int OPITCH = D + 4;                             // floats
     static constexpr int EPI_BYTES = 2 * ROWS_PAD * OPITCH * 4 + 2 * 4 * ROWS_PAD * 4;
@@ -191,10 +207,30 @@ struct Cfg {
     static constexpr int IPS = 32 / TPI;          // load instructions per 32-token step
     // Workgroups per compute unit the register allocation is held to. The loop
     // keeps one slice of K or V in flight per wave, so resident waves are what
-    // hides HBM latency; these configurations fit 3 waves per SIMD (<= 168
-    // VGPRs) without spilling the loop.
-    static constexpr int MINB = (KV == KV_FP8 && VT && D == 128 && NT == 1) || KV == KV_MXFP4 ? 3 : 1;
+    // hides HBM latency. These configurations fit 3 (<= 168 VGPRs) or 2
+    // (<= 256) waves per SIMD without spilling the loop.
+    static constexpr int MINB = (KV == KV_FP8 && VT && D == 128 && NT == 1) || KV == KV_MXFP4 ? 3
+                                : (KV == KV_BF16 && VDMA && D == 128 && NT == 1)              ? 2
+                                                                                              : 1;
+    // vector-memory instructions load_k issues (the explicit wait before PV counts them)
+    static constexpr int KVMEM = 4 * KLOADS + (KV == KV_MXFP4 ? 4 : 0) + (SC == SC_TOKEN ? 8 : 0);
 };
+
+// Chunk swizzle of the DMA'd V tile: row r (slice token r) stores its 16-byte
+// chunk c at position c ^ vswz(r). Chosen so that the 32 lanes of a half-wave
+// reading one PV fragment touch 64 distinct LDS banks:
+//   bf16 (ds_read_b64_tr_b16): a half-wave reads 32 bytes of rows
+//     16g + 8s + [0, 4) (+ 4) for g in {2h, 2h + 1}; the XOR moves bits 1..3
+//     of the chunk by (r & 3) and bit 4 of r;
+//   e4m3 (ds_read_b64_tr_b8): a half-wave reads 16 bytes of rows
+//     16g + 8s + [0, 8); with 256-byte rows the XOR is (r & 7) and bit 4 of r,
+//     with 128-byte rows (two rows per 64 banks) it is ((r >> 1) & 3) and bit 4.
+template <class C>
+PA_DEV int vswz(int r) {
+    if constexpr (C::KV == KV_BF16) return 2 * ((r & 3) | (((r >> 4) & 1) << 2));
+    else if constexpr (C::ROWB >= 256) return (r & 7) | (((r >> 4) & 1) << 3);
+    else return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+}
 
 template <class C>
 struct State {
@@ -451,9 +487,28 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
 }
 
 template <class C>
-PA_DEV void load_v(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, VBuf<C>& vb) {
+PA_DEV void load_v(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, VBuf<C>& vb, char* vlds) {
     constexpr int PG = C::PG;
     const int ln = cx.ln, lg = cx.lg, lane = cx.lane;
+    if constexpr (C::VDMA) {
+        // instruction i fills LDS bytes [1024 i, 1024 i + 1024) of the wave's
+        // tile: rows i * RPI + lane / CPR, chunk position lane % CPR; whole rows
+        // per lane group, so the loads are nontemporal
+        constexpr int RPI = 64 / C::CPR;
+#pragma unroll
+        for (int i = 0; i < C::CPR; ++i) {
+            const int r = i * RPI + lane / C::CPR;
+            const int c = (lane % C::CPR) ^ vswz<C>(r);
+            const int vpage = sp.pg[C::NPC == 1 ? 0 : (i * RPI) / PG];  // uniform per instruction
+            const long row = (long)vpage * a.num_kv_heads * PG + slot_in_page(sp, r);
+            __builtin_amdgcn_global_load_lds((const void*)(cx.vbase + row * C::ROWB + 16 * c),
+                                             (__attribute__((address_space(3))) void*)(vlds + 1024 * i), 16, 0,
+                                             kLoadNontemporal);
+        }
+        // nothing moves across: the wait before PV counts the vector-memory
+        // instructions issued after these
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (C::STAGE_V) {
         // step s stages slice tokens 16*(e>>3) + 8s + (e&7), e in [0, 32)
         const int vseg = lane % C::LPR;
@@ -590,8 +645,16 @@ PA_DEV void wave_lds_sync() {
 }
 
 // V operand preparation (boundary mask) and O^T[d][row] += V^T . P^T.
-template <class C, bool MASK>
-PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& st, int cb, char* vlds) {
+// VM_AFTER: vector-memory instructions issued between this slice's V DMA and
+// this call (the next slice's K loads in the loop, none in the tail).
+//
+// The compiler's own wait for LDS written by DMA is vmcnt(0), which would also
+// wait for the next slice's K loads; vlds is restrict-qualified here so that it
+// leaves these reads alone, and the explicit wait below orders them after the
+// DMA instead (the sched barriers pin the instruction order it counts on).
+template <class C, bool MASK, int VM_AFTER>
+PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& st, int cb,
+               char* __restrict__ vlds) {
     constexpr int NT = C::NT;
     const int ln = cx.ln, lg = cx.lg, lane = cx.lane;
     u32x4 vt[C::VT ? C::DT : 1][C::VT ? (C::ESZ == 2 ? 2 : 1) : 1];
@@ -614,6 +677,11 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
                     for (int dt = 0; dt < C::DT; ++dt) vt[dt][w][j] &= mk;
                 }
         }
+    }
+    if constexpr (C::VDMA) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_AFTER));  // this slice's V is in LDS
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -652,7 +720,42 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
             bf16x8 va;
-            if constexpr (C::STAGE_V) {
+            if constexpr (C::VDMA && C::KV == KV_BF16) {
+                // A lane (m, g) needs V[16g + 8s + e][16dt + m], e in [0, 8): two
+                // transposed reads; source lane ln reads row 16g + 8s + (ln >> 2)
+                // (+ 4), columns 16dt + 4 (ln & 3) + [0, 4)
+                const int r0 = 16 * lg + 8 * s + (ln >> 2);
+                const int c = 2 * dt + ((ln & 3) >> 1);
+                const char* base = vlds + r0 * C::ROWB + 16 * (c ^ vswz<C>(r0)) + 8 * (ln & 1);
+                // vswz is the same for r0 and r0 + 4
+                bf16x4 r0v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base));
+                bf16x4 r1v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(base + 4 * C::ROWB));
+                u32x4 w = __builtin_bit_cast(u32x4, bf16x8{r0v[0], r0v[1], r0v[2], r0v[3], r1v[0], r1v[1], r1v[2], r1v[3]});
+                if (MASK) {
+                    // element e is token cb + 16g + 8s + e: zero those at or past L (PR #7092, "Fix")
+                    const int valid = cx.L - (cb + 16 * lg + 8 * s);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        w[j] &= (valid > 2 * j ? 0x0000FFFFu : 0u) | (valid > 2 * j + 1 ? 0xFFFF0000u : 0u);
+                }
+                va = as_bf16x8(w);
+            } else if constexpr (C::VDMA) {
+                // e4m3: one transposed byte read gives lane (m, g) the 8 bytes
+                // V[16g + 8s + e][16dt + m]; source lane ln reads 8 bytes of row
+                // 16g + 8s + (ln >> 1) at column 16dt + 8 (ln & 1)
+                const int r = 16 * lg + 8 * s + (ln >> 1);
+                const char* base = vlds + r * C::ROWB + 16 * (dt ^ vswz<C>(r)) + 8 * (ln & 1);
+                typedef int i32x2 __attribute__((ext_vector_type(2)));
+                i32x2 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(base));
+                uint32_t b0 = (uint32_t)b[0], b1 = (uint32_t)b[1];
+                if (MASK) {
+                    const int valid = cx.L - (cb + 16 * lg + 8 * s);  // byte e is token cb + 16g + 8s + e
+                    b0 &= keep_bytes(valid);
+                    b1 &= keep_bytes(valid - 4);
+                }
+                va = fp8x8_to_bf16x8(b0, b1);
+            } else if constexpr (C::STAGE_V) {
                 // A lane (m = d offset, g) needs rows 8g + [0, 8) at column 16dt + m
                 const char* base = vlds + (8 * lg + (ln >> 2)) * C::VPITCH + 2 * (16 * dt + 4 * (ln & 3));
                 bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -752,18 +855,18 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
         VBuf<C> vb;
         load_k<C>(a, cx, sp, kb);
         for (int j = 0; j + 1 < total; ++j) {  // full tiles followed by another tile
-            load_v<C>(a, cx, sp, vb);
+            load_v<C>(a, cx, sp, vb, vlds);
             PFrag<C> pf;
             qk_softmax<C, false>(a, cx, qf, kb, st, pf, cb);
             sp = slice_pages<C>(a, cx, pc, tb + j + 1);
             load_k<C>(a, cx, sp, kb);
-            pv<C, false>(cx, vb, pf, st, cb, vlds);
+            pv<C, false, C::KVMEM>(cx, vb, pf, st, cb, vlds);
             cb += kTileTokens;
         }
-        load_v<C>(a, cx, sp, vb);
+        load_v<C>(a, cx, sp, vb, vlds);
         PFrag<C> pf;
         qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb);
-        pv<C, true>(cx, vb, pf, st, cb, vlds);
+        pv<C, true, 0>(cx, vb, pf, st, cb, vlds);
     }
 
     // ---- merge the four waves (fixed order), then store
