@@ -486,6 +486,20 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
     }
 }
 
+// Before a slice's V DMA: wait for everything outstanding (this slice's K).
+// The compiler does not count LDS DMA instructions when it computes its own
+// waits, so the wait it would put before QK for K loads issued ahead of the
+// DMA is vmcnt(0), which also waits for the DMA just issued; waiting here
+// instead lets the V transfer overlap QK.
+template <class C>
+PA_DEV void dma_fence() {
+    if constexpr (C::VDMA) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <class C>
 PA_DEV void load_v(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, VBuf<C>& vb, char* vlds) {
     constexpr int PG = C::PG;
@@ -855,6 +869,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
         VBuf<C> vb;
         load_k<C>(a, cx, sp, kb);
         for (int j = 0; j + 1 < total; ++j) {  // full tiles followed by another tile
+            dma_fence<C>();
             load_v<C>(a, cx, sp, vb, vlds);
             PFrag<C> pf;
             qk_softmax<C, false>(a, cx, qf, kb, st, pf, cb);
@@ -863,6 +878,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
             pv<C, false, C::KVMEM>(cx, vb, pf, st, cb, vlds);
             cb += kTileTokens;
         }
+        dma_fence<C>();
         load_v<C>(a, cx, sp, vb, vlds);
         PFrag<C> pf;
         qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb);
