@@ -24,7 +24,7 @@ With --all, every workload is also timed one call at a time with the cold-cache
 protocol: a 1 GiB buffer is read before each call (the last-level cache is
 256 MB; a read leaves clean lines, where a write would leave dirty lines for
 the decode to write back), and the median of the per-call event times is
-reported.
+reported, for pa_decode with its plan and for the plan-free pa_decode_direct.
 """
 from __future__ import annotations
 
@@ -185,6 +185,21 @@ def time_all(steps, warmup):
             b.record()
         torch.cuda.synchronize()
         us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+        prob = pa.problem_of(case)
+
+        def call_direct():
+            pa.pa_decode_direct(prob, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
+                                d["block_tables"], d["context_lens"], out)
+
+        for _ in range(warmup):
+            call_direct()
+        for a, b in ev:
+            torch.amax(flush, dim=0, out=flush_out)
+            a.record()
+            call_direct()
+            b.record()
+        torch.cuda.synchronize()
+        us_direct = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
         plan.set_timing(True, steps)
         for _ in range(steps):
             call()
@@ -198,9 +213,11 @@ def time_all(steps, warmup):
                            "merge_us": round(m_ms / n * 1e3, 2) if inf.merge_needed else 0.0,
                            "kv_bytes": nbytes, "kv_GBps": round(gbps, 1),
                            "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1),
-                           "tasks": inf.num_tasks, "slots": inf.slots, "partitions_max": inf.max_parts}
-        print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  tile %8.2f us  tasks %5d slots %4d" % (
-            spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, t_ms / n * 1e3, inf.num_tasks, inf.slots),
+                           "tasks": inf.num_tasks, "slots": inf.slots, "partitions_max": inf.max_parts,
+                           "plan_free_us_per_call": round(us_direct, 2),
+                           "plan_free_pct_of_hbm_peak": round(100 * nbytes / (us_direct * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  tile %8.2f us  tasks %5d slots %4d  plan-free %8.2f us" % (
+            spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, t_ms / n * 1e3, inf.num_tasks, inf.slots, us_direct),
             file=sys.stderr, flush=True)
         del d, plan, out, case
         torch.cuda.empty_cache()

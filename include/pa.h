@@ -169,6 +169,28 @@ pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_ca
                     const void* k_scale, const void* v_scale, const int32_t* block_tables,
                     const int32_t* context_lens, void* out, pa_stream_t stream);
 
+/*
+ * pa_decode_direct -- plan-free decode: one task per (sequence, KV head),
+ * derived from the workgroup index, over every tile of the sequence up to the
+ * device context length; each task normalizes and stores its output rows
+ * itself, so there is no plan, no partition reduce, no workspace and no host
+ * copy of the lengths (ROCm/aiter PR #7056, "Bandwidth": the plan-free mode
+ * whose tasks follow from the block index, and the direct output of a plan
+ * with one partition). The result is bitwise equal to pa_decode with a plan of
+ * max_partitions == 1 for the same problem. Context-0 rows are written as 0.
+ *
+ * Suited to batches with many short sequences: a long sequence is one
+ * workgroup's serial work here, where pa_plan would split it.
+ *
+ * Arguments, layouts and device-side guarantees are those of pa_decode; the
+ * problem descriptor's max_partitions and task_budget are ignored. Validates
+ * the problem and probes the device on every call (the probe is cached per
+ * process), allocates nothing and does not synchronize.
+ */
+pa_status pa_decode_direct(const pa_problem* problem, const void* query, const void* key_cache,
+                           const void* value_cache, const void* k_scale, const void* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, void* out, pa_stream_t stream);
+
 /* Release a plan and its device workspace (NULL-safe). Synchronizes the device. */
 void pa_plan_destroy(pa_plan_t* plan);
 

@@ -47,7 +47,7 @@ class pa_plan_info(ctypes.Structure):
         "num_tasks", "max_parts", "total_parts", "tiles_per_task", "merge_needed", "num_cus", "slots")]
 
 
-EXPORTS = ["pa_plan", "pa_decode", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
+EXPORTS = ["pa_plan", "pa_decode", "pa_decode_direct", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
            "pa_plan_host", "pa_plan_set_timing", "pa_plan_read_timing", "pa_last_error", "pa_version"]
 
 _lib = None
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.pa_plan.argtypes = [P(pa_problem), vp, vp, P(vp)]
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode.argtypes = [vp] * 10
+    L.pa_decode_direct.restype = ctypes.c_int
+    L.pa_decode_direct.argtypes = [P(pa_problem)] + [vp] * 9
     L.pa_plan_destroy.restype = None
     L.pa_plan_destroy.argtypes = [vp]
     L.pa_plan_workspace_bytes.restype = ctypes.c_size_t
@@ -199,6 +201,22 @@ def pa_decode(plan: Plan, query, key_cache, value_cache, k_scale, v_scale, block
                          _dev(v_scale, "v_scale", True), _dev(block_tables, "block_tables"),
                          _dev(context_lens, "context_lens"), _dev(out, "out"),
                          ctypes.c_void_p(_stream_ptr(stream)))
+    _check(st)
+    return out
+
+
+def pa_decode_direct(problem: pa_problem, query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                     context_lens, out, stream=None):
+    """Plan-free decode (one task per sequence and KV head); enqueued on `stream`."""
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16")
+    st = lib().pa_decode_direct(ctypes.byref(problem), _dev(query, "query"), _dev(key_cache, "key_cache"),
+                                _dev(value_cache, "value_cache"), _dev(k_scale, "k_scale", True),
+                                _dev(v_scale, "v_scale", True), _dev(block_tables, "block_tables"),
+                                _dev(context_lens, "context_lens"), _dev(out, "out"),
+                                ctypes.c_void_p(_stream_ptr(stream)))
     _check(st)
     return out
 

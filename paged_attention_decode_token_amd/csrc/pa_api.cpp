@@ -152,16 +152,23 @@ static void partition_counts(const std::vector<int>& tiles, int tpt, int max_par
 
 // Estimated completion time (seconds) of a task set launched longest first on
 // `slots` workgroup slots. Running workgroups share the memory system: each
-// streams at min(kWgBytesPerS, kHbmBytesPerS / running), where a workgroup on
-// its own is latency-bound at about one 256-token tile per kTileS (its four
-// waves keep one slice of K or V in flight each; measured 4-6 us per tile on
-// bf16, fp8 and MXFP4 caches alike). A task costs its KV bytes plus a fixed
-// start/epilogue time; any split sequence adds the merge launch.
+// streams at min(kWgBytesPerS, kHbmBytesPerS / running). A workgroup on its own
+// is bound by its latency, about one 256-token tile per kTileS (its four waves
+// keep one slice of K or V in flight each), and by what one compute unit
+// streams, about 25 GB/s (6.4 TB/s over 256 CUs): a bf16 tile of 128 KB takes
+// 5.2 us at that rate, an fp8 transposed-V tile of 64 KB 2.8 us, an MXFP4 tile
+// of 35 KB 2 us on its own (measured on the workloads of the benchmark). A task
+// costs its KV bytes plus a fixed start/epilogue time; any split sequence adds
+// the merge launch.
 static double plan_cost(const std::vector<int>& tiles, const std::vector<int>& parts, int H, int slots,
-                        double tile_bytes, double partial_bytes, long* ntasks_out) {
-    const double kHbmBytesPerS = 6.5e12;  // sustained HBM read rate of the tile kernel
-    const double kTileS = 5.5e-6;         // one workgroup, one tile, latency-bound
-    const double kWgBytesPerS = tile_bytes / kTileS;
+                        double tile_bytes, double partial_bytes, bool half_rows, long* ntasks_out) {
+    // sustained HBM read rate of the tile kernel; transposed V rows are read
+    // half by one wave and half by the next, which streams slower (5.3-5.8
+    // TB/s for that pattern against 6.1-6.9 for whole rows, measured)
+    const double kHbmBytesPerS = half_rows ? 5.9e12 : 6.4e12;
+    const double kCuBytesPerS = 2.5e10;   // one compute unit
+    const double kTileS = 2.8e-6;         // one workgroup, one tile, latency-bound
+    const double kWgBytesPerS = std::min(kCuBytesPerS, tile_bytes / kTileS);
     const double kTaskS = 1.0e-6;         // start + four-wave merge + store of one task
     const double kMergeS = 8.0e-6;        // merge kernel (about 4.5 us) and the gap between the launches
     std::vector<double> bytes;
@@ -249,12 +256,13 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int 
         long nt = 0;
         const double tb = tile_bytes_of(p);
         const double pbytes = (double)rows_of(p) * (p.head_dim + 2) * 4.0;  // one task's partial (O, m, l)
-        double best = plan_cost(tiles, parts, H, slots, tb, pbytes, &nt);
+        const bool half_rows = p.v_layout == PA_V_TRANSPOSED;
+        double best = plan_cost(tiles, parts, H, slots, tb, pbytes, half_rows, &nt);
         std::vector<int> cand;
         for (int t = tmax - 1; t >= 1; --t) {
             partition_counts(tiles, t, max_parts, &cand);
             if (cand == parts) continue;
-            double c = plan_cost(tiles, cand, H, slots, tb, pbytes, &nt);
+            double c = plan_cost(tiles, cand, H, slots, tb, pbytes, half_rows, &nt);
             if (nt > 8L * slots) break;
             if (c < best * 0.995) {
                 best = c;
@@ -426,12 +434,10 @@ pa_status pa_plan_get_info(const pa_plan_t* p, pa_plan_info* info) {
 
 static bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
 
-pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_cache, const void* value_cache,
-                    const void* k_scale, const void* v_scale, const int32_t* block_tables,
-                    const int32_t* context_lens, void* out, pa_stream_t stream) {
-    if (!plan) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
-    const pa_problem& p = plan->prob;
-    if (p.num_seqs == 0) return PA_OK;
+// Pointer checks shared by the planned and the plan-free decode.
+static pa_status check_pointers(const pa_problem& p, const void* query, const void* key_cache,
+                                const void* value_cache, const void* k_scale, const void* v_scale,
+                                const int32_t* block_tables, const int32_t* context_lens, const void* out) {
     if (!query || !key_cache || !value_cache || !block_tables || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
     if (misaligned(query) || misaligned(key_cache) || misaligned(value_cache) || misaligned(out))
@@ -443,6 +449,17 @@ pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_ca
     if (need_scales && (misaligned(k_scale) || misaligned(v_scale)) &&
         !(p.scale_mode == PA_SCALE_PER_TENSOR && !((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u)))
         return fail(PA_ERR_INVALID_ARG, "scale tables must be 16-byte aligned (per-tensor scales: 4-byte)");
+    return PA_OK;
+}
+
+pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_cache, const void* value_cache,
+                    const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                    const int32_t* context_lens, void* out, pa_stream_t stream) {
+    if (!plan) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+    const pa_problem& p = plan->prob;
+    if (p.num_seqs == 0) return PA_OK;
+    pa_status st = check_pointers(p, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, out);
+    if (st != PA_OK) return st;
     hipError_t e = hipSetDevice(plan->device);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "hipSetDevice failed: %s", hipGetErrorString(e));
 
@@ -468,6 +485,7 @@ pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_ca
     a.num_blocks = p.num_blocks;
     const double sm = p.softmax_scale != 0.f ? (double)p.softmax_scale : 1.0 / std::sqrt((double)p.head_dim);
     a.scale_log2 = (float)(sm * 1.4426950408889634);
+    a.plan_free = 0;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     pa_plan_t* mp = const_cast<pa_plan_t*>(plan);
@@ -485,6 +503,54 @@ pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_ca
         if ((e = hipEventRecord(ev[2], s)) != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
         mp->ncalls++;
     }
+    return PA_OK;
+}
+
+pa_status pa_decode_direct(const pa_problem* problem, const void* query, const void* key_cache,
+                           const void* value_cache, const void* k_scale, const void* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, void* out, pa_stream_t stream) {
+    pa_status st = validate(problem);
+    if (st != PA_OK) return st;
+    const pa_problem& p = *problem;
+    if (p.num_seqs == 0) return PA_OK;
+    if ((long)p.num_seqs * p.num_kv_heads > 0x7FFFFFFFL)
+        return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads exceeds the grid");
+    st = check_pointers(p, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, out);
+    if (st != PA_OK) return st;
+    DeviceInfo dev;
+    st = probe_device(&dev);
+    if (st != PA_OK) return st;
+    if (!dev.gfx950) return fail(PA_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 only", dev.device, dev.arch.c_str());
+    const pa::KernelKey key = key_of(p);
+    if (!pa::have_tile_kernel(key)) return fail(PA_ERR_UNSUPPORTED, "no kernel instance for this problem");
+    hipError_t e = hipSetDevice(dev.device);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipSetDevice failed: %s", hipGetErrorString(e));
+
+    pa::TileArgs a{};
+    a.q = query;
+    a.k = key_cache;
+    a.v = value_cache;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.tasks = nullptr;
+    a.seq_parts = nullptr;
+    a.part_ml = nullptr;
+    a.part_o = nullptr;
+    a.num_seqs = p.num_seqs;
+    a.qlen = p.qlen;
+    a.num_kv_heads = p.num_kv_heads;
+    a.q_per_kv = p.q_per_kv;
+    a.rows = rows_of(p);
+    a.max_blocks = p.max_blocks_per_seq;
+    a.num_blocks = p.num_blocks;
+    const double sm = p.softmax_scale != 0.f ? (double)p.softmax_scale : 1.0 / std::sqrt((double)p.head_dim);
+    a.scale_log2 = (float)(sm * 1.4426950408889634);
+    a.plan_free = 1;
+    e = pa::launch_tile(key, a, p.num_seqs * p.num_kv_heads, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "tile kernel launch failed: %s", hipGetErrorString(e));
     return PA_OK;
 }
 

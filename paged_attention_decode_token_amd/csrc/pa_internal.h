@@ -32,6 +32,7 @@ struct TileArgs {
     float* part_o;             // [slots][Hkv][rows][D]: unnormalised weighted sum of V
     int32_t num_seqs, qlen, num_kv_heads, q_per_kv, rows, max_blocks, num_blocks;
     float scale_log2;  // softmax_scale * log2(e)
+    int32_t plan_free;  // 1: one task per (sequence, KV head) from the block index, tasks unused
 };
 
 struct KernelKey {

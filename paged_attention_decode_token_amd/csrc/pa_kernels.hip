@@ -802,18 +802,32 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     cx.wave = uniform(threadIdx.x >> 6);
     cx.ln = cx.lane & 15;
     cx.lg = cx.lane >> 4;
-    const int* task = a.tasks + 4 * blockIdx.x;
-    cx.b = uniform(task[0]);
-    const int kp = uniform(task[1]);
-    cx.kvh = kp & 0xFFFF;
-    const int part = kp >> 16;
-    const int tb = uniform(task[2]);
+    // A planned launch reads its task (sequence, KV head | partition << 16,
+    // tile range) from the plan; a plan-free launch derives it from the block
+    // index: one task per (sequence, KV head) over all of its tiles, stored
+    // directly (PR #7056, "Bandwidth": tasks follow from the block index).
+    int part, tb, te_task;
+    if (a.plan_free) {
+        cx.b = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
+        cx.kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
+        part = 0;
+        tb = 0;
+        te_task = 0x7FFFFFFF;
+    } else {
+        const int* task = a.tasks + 4 * blockIdx.x;
+        cx.b = uniform(task[0]);
+        const int kp = uniform(task[1]);
+        cx.kvh = kp & 0xFFFF;
+        part = kp >> 16;
+        tb = uniform(task[2]);
+        te_task = uniform(task[3]);
+    }
     int L = uniform(a.context_lens[cx.b]);
     L = L < 0 ? 0 : L;
     L = L > a.max_blocks * PG ? a.max_blocks * PG : L;
     cx.L = L;
     const int ntiles = (L + kTileTokens - 1) / kTileTokens;
-    const int te = min(uniform(task[3]), ntiles);
+    const int te = min(te_task, ntiles);
     cx.npages = (L + PG - 1) / PG;
     cx.bt_row = a.block_tables + (long)cx.b * a.max_blocks;
     const long head_bytes = C::PAGE_BYTES_HEAD;
@@ -952,7 +966,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] += *reinterpret_cast<f32x4*>(obuf_at(0, nt, dt));
 
-    const int nparts = a.seq_parts[2 * cx.b];
+    const int nparts = a.plan_free ? 1 : a.seq_parts[2 * cx.b];
     const int Hq = a.num_kv_heads * a.q_per_kv;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {

@@ -61,6 +61,20 @@ def test_refusals(kw, status):
     assert B.pa_last_error()
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=32), B.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype="mxfp4", page_size=128, qlen=2), B.PA_ERR_UNSUPPORTED),
+    (dict(qlen=0), B.PA_ERR_INVALID_ARG),
+    (dict(), B.PA_ERR_INVALID_ARG),  # a valid problem with NULL pointers
+])
+def test_plan_free_refusals_come_before_the_device(kw, status):
+    """pa_decode_direct validates the descriptor, then the pointers, and only
+    then probes the device: every refusal here returns on a host without one."""
+    st = B.lib().pa_decode_direct(B.ctypes.byref(_prob(**kw)), *([None] * 9))
+    assert st == status
+    assert B.pa_last_error()
+
+
 def test_host_length_checks():
     with pytest.raises(B.PaError):
         B.pa_plan_host(_prob(), [10, -1, 30, 40])

@@ -175,3 +175,52 @@ def test_mxfp4_scaled_qk_mode(spec):
     assert rel <= REL_L2
     zero = run(I.refill(case, "zero"), mxfp4_scaled_qk=1)[0]
     assert torch.equal(zero.view(torch.int16), out.view(torch.int16))
+
+
+# ------------------------------------------------------------- plan-free path
+
+def run_direct(case, fill_out=float("nan")):
+    """pa_decode_direct on a Case (no plan); returns the bf16 output."""
+    d = B.device_tensors(case)
+    out = torch.full((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), fill_out, dtype=torch.bfloat16,
+                     device="cuda")
+    B.pa_decode_direct(B.problem_of(case), d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
+                       d["block_tables"], d["context_lens"], out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_plan_free_equals_one_partition_plan_and_oracle(spec):
+    """The plan-free decode is bitwise equal to a plan with one partition per
+    sequence (ROCm/aiter PR #7056, "Bandwidth") and meets the parity bar."""
+    case = I.make_case(spec)
+    direct = run_direct(case)
+    planned, plan = run(case, max_partitions=1)
+    assert plan.info().merge_needed == 0
+    assert torch.equal(direct.view(torch.int16), planned.view(torch.int16))
+    check_parity(direct, oracle.pa_decode(case), what=spec.name + " plan-free")
+
+
+@pytest.mark.parametrize("base", [I.TINY_BF16, I.BF16_P64, I.FP8TOK_Q4, I.FP8_TRANS, I.MXFP4_SHORT_QBF],
+                         ids=lambda s: s.name)
+def test_plan_free_edge_lengths_and_poison(base):
+    spec = base.replace(name=base.name + "_edges", num_seqs=len(EDGE_LENS), lens=("fixed", EDGE_LENS),
+                        num_kv_heads=min(base.num_kv_heads, 2))
+    case = I.make_case(spec, fill="zero")
+    out = run_direct(case)
+    check_parity(out, oracle.pa_decode(case), what=spec.name + " plan-free")
+    assert torch.all(out[0].float().cpu() == 0)  # L = 0 rows are written as zeros
+    for fill in ("nan", "inf", "random"):
+        assert torch.equal(run_direct(I.refill(case, fill)).view(torch.int16), out.view(torch.int16)), fill
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("spec", I.FULL, ids=lambda s: s.name)
+def test_plan_free_full_size(spec):
+    case = I.make_case(spec)
+    out = run_direct(case)
+    seqs = list(range(case.num_seqs)) if case.num_seqs <= 4 else [0, 1, case.num_seqs // 2, case.num_seqs - 1]
+    check_parity(out, oracle.pa_decode(case, seqs=seqs), seqs=seqs, what=spec.name + " plan-free (sampled)")
+    planned, _ = run(case, max_partitions=1)
+    assert torch.equal(out.view(torch.int16), planned.view(torch.int16))
