@@ -47,6 +47,8 @@ class OracleProblem(ctypes.Structure):
         ("v_layout", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_double),
+        ("causal", ctypes.c_int32),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -128,7 +130,8 @@ def pa_decode(case, seqs=None, t_begin=0, t_end=-1, nthreads=0, with_lse=False):
         head_dim=case.head_dim, page_size=case.page_size, num_blocks=case.num_blocks,
         max_blocks_per_seq=case.max_blocks_per_seq, kv_dtype=KV_DTYPES[case.kv_dtype],
         scale_mode=SCALE_MODES[case.scale_mode], v_layout=V_LAYOUTS[case.v_layout], q_dtype=Q_DTYPES[case.q_dtype],
-        softmax_scale=float(case.softmax_scale or 0.0))
+        softmax_scale=float(case.softmax_scale or 0.0), causal=int(getattr(case, "causal", 0)),
+        window=int(getattr(case, "window", 0)))
     arrs = [_np(case.query), _np(case.key_cache), _np(case.value_cache), _np(case.k_scale), _np(case.v_scale),
             _np(case.block_tables).astype(np.int32), _np(case.context_lens).astype(np.int32)]
     Hq = case.num_kv_heads * case.q_per_kv

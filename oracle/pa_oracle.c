@@ -33,7 +33,13 @@
  *     with max|q| <= 448 * 2^e (e = 0 for an all-zero row), round to nearest
  *     even with saturation to +-448, and the logits are multiplied by 2^e;
  *   - an e4m3 query is used as stored, with unit scale;
- *   - with qlen > 1 every query row attends to all of [0, L_b) (no causal mask).
+ *   - with qlen > 1 every query row attends to all of [0, L_b) unless the
+ *     problem asks for causal attention;
+ *   - causal attention (query tokens are the last qlen positions of the
+ *     sequence, their K/V already in the cache): query token i attends to
+ *     t < e_i = L_b - qlen + i + 1; otherwise e_i = L_b;
+ *   - a sliding window of W > 0 tokens keeps t >= e_i - W as well, so query
+ *     token i attends to [max(0, e_i - W), e_i); an empty range gives o = 0.
  *
  * Parity pins live in the test suite: brute-force dense attention, softmax
  * normalisation, context_len = 1, split/merge invariance, page-permutation
@@ -56,6 +62,8 @@ typedef struct {
     int32_t v_layout;   /* 0 plain [blocks][kvh][page][D], 1 transposed [blocks][kvh][D][page] */
     int32_t q_dtype;    /* 0 bf16, 1 e4m3fn */
     double softmax_scale;
+    int32_t causal;     /* 1: query token i attends to t < L - qlen + i + 1 */
+    int32_t window;     /* > 0: and to t >= (that end) - window; 0: no window */
 } oracle_problem;
 
 enum { OR_OK = 0, OR_EINVAL = 1 };
@@ -216,8 +224,9 @@ static double token_scale(const oracle_problem* p, const void* scale, int64_t pa
 
 /*
  * oracle_pa_decode: attention of every selected sequence over its tokens
- * [t_begin, min(t_end, L_b)). With t_begin = 0 and t_end < 0 the range is the
- * whole context. out: fp64 [num_seqs][qlen][Hq][D], normalised over the range
+ * [t_begin, min(t_end, L_b)), intersected for query token i with its causal /
+ * sliding-window range [s_i, e_i). With t_begin = 0 and t_end < 0 the range is
+ * the whole context. out: fp64 [num_seqs][qlen][Hq][D], normalised over the range
  * (0 for an empty range). lse (nullable): fp64 [num_seqs][qlen][Hq], the
  * natural log of sum_t exp(s_t) over the range (-inf for an empty range).
  * seqs (nullable): the sequence indices to compute; rows of other sequences
@@ -229,7 +238,8 @@ int oracle_pa_decode(const oracle_problem* p, const void* query, const void* key
                      int32_t t_end, double* out, double* lse, int32_t nthreads)
 {
     if (!p || p->num_seqs < 0 || p->qlen < 1 || p->num_kv_heads < 1 || p->q_per_kv < 1 || p->head_dim < 1 ||
-        p->page_size < 1 || p->max_blocks_per_seq < 0 || p->num_blocks < 1)
+        p->page_size < 1 || p->max_blocks_per_seq < 0 || p->num_blocks < 1 || p->window < 0 ||
+        (p->causal != 0 && p->causal != 1))
         return OR_EINVAL;
     if (p->kv_dtype == 2 && (p->head_dim % 32) != 0)
         return OR_EINVAL;
@@ -251,13 +261,18 @@ int oracle_pa_decode(const oracle_problem* p, const void* query, const void* key
         int b = seqs ? seqs[pair / H] : pair / H;
         int kvh = pair % H;
         int L = context_lens[b];
-        int t0 = t_begin < 0 ? 0 : t_begin;
-        int t1 = (t_end < 0 || t_end > L) ? L : t_end;
-        int n = t1 > t0 ? t1 - t0 : 0;
+        int r0 = t_begin < 0 ? 0 : t_begin;
+        int r1 = (t_end < 0 || t_end > L) ? L : t_end;
         double* qhat = (double*)malloc(sizeof(double) * (size_t)D);
-        double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
         double* acc = (double*)malloc(sizeof(double) * (size_t)D);
         for (int i = 0; i < QL; i++) {
+            /* this query token's tokens: [s_i, e_i) within [r0, r1) */
+            int e_i = p->causal ? L - QL + i + 1 : L;
+            int s_i = p->window > 0 ? e_i - p->window : 0;
+            int t0 = s_i > r0 ? s_i : r0;
+            int t1 = e_i < r1 ? e_i : r1;
+            int n = t1 > t0 ? t1 - t0 : 0;
             for (int hg = 0; hg < G; hg++) {
                 int h = kvh * G + hg;
                 int64_t row = ((int64_t)b * QL + i) * Hq + h;

@@ -50,6 +50,8 @@ class Spec:
     fill: str = "nan"  # nan | inf | zero | random
     seed: int = 0
     pad_cols: int = 2
+    causal: int = 0  # 1: query token i attends to t < L - qlen + i + 1
+    window: int = 0  # > 0: sliding window of that many tokens ending there
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -79,6 +81,8 @@ class Case:
     v_scale: Optional[torch.Tensor]
     block_tables: torch.Tensor
     context_lens: torch.Tensor
+    causal: int = 0
+    window: int = 0
 
     @property
     def num_q_heads(self) -> int:
@@ -292,7 +296,8 @@ def make_case(spec: Spec, fill: Optional[str] = None, seed: Optional[int] = None
                 num_blocks=num_blocks, max_blocks_per_seq=width, max_context_len=max(lens + [0]),
                 kv_dtype=spec.kv_dtype, scale_mode=spec.scale_mode, v_layout=spec.v_layout, q_dtype=spec.q_dtype,
                 softmax_scale=0.0, query=query, key_cache=K, value_cache=V, k_scale=k_scale, v_scale=v_scale,
-                block_tables=bt, context_lens=torch.tensor(lens, dtype=torch.int32))
+                block_tables=bt, context_lens=torch.tensor(lens, dtype=torch.int32), causal=spec.causal,
+                window=spec.window)
 
 
 def _unowned_pairs(bt, lens, PG):

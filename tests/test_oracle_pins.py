@@ -10,6 +10,7 @@ Each test names what fixes the expected value:
 Negative controls check that a plausible mistake in the reference (wrong GQA
 grouping, scale off by 5 %, transposed V read as plain) is caught.
 """
+import dataclasses
 import math
 import os
 
@@ -161,7 +162,8 @@ def _deq_rows(case, cache, scale, pages, kvh, transposed, mx_scale=None, nibble_
     return vals
 
 
-def dense_reference(case, gqa=lambda h, G, H: h // G, sigma_mult=1.0, v_transposed=None, nibble_swap=False):
+def dense_reference(case, gqa=lambda h, G, H: h // G, sigma_mult=1.0, v_transposed=None, nibble_swap=False,
+                    causal_shift=0):
     B, QL, H, G, D, PG = case.num_seqs, case.qlen, case.num_kv_heads, case.q_per_kv, case.head_dim, case.page_size
     Hq = H * G
     sigma = sigma_mult / math.sqrt(D)
@@ -201,7 +203,19 @@ def dense_reference(case, gqa=lambda h, G, H: h // G, sigma_mult=1.0, v_transpos
                         q8 = torch.from_numpy(q / 2.0 ** e).to(torch.float8_e4m3fn).to(torch.float64).numpy()
                         q = q8 * 2.0 ** e
                 s = (K @ q) * sigma
-                w = np.exp(s - s.max())
+                # query token i sits at position L - qlen + i when causal; a
+                # window keeps the last `window` positions up to and including it
+                pos = np.arange(L)
+                keep = np.ones(L, dtype=bool)
+                last = (L - QL + i + causal_shift) if case.causal else L - 1
+                if case.causal:
+                    keep &= pos <= last
+                if case.window > 0:
+                    keep &= pos > last - case.window
+                if not keep.any():
+                    continue
+                s = np.where(keep, s, -np.inf)
+                w = np.exp(s - s[keep].max())
                 out[b, i, h] = (w / w.sum()) @ V
     return out
 
@@ -391,3 +405,79 @@ def test_qlen_rows_are_independent_non_causal():
         single = _with(case, qlen=1, query=case.query[:, i:i + 1].contiguous())
         o1 = oracle.pa_decode(single)
         assert np.array_equal(out[:, i], o1[:, 0])
+
+
+# ------------------------------------------------ causal and sliding window
+
+MASK_SPECS = [
+    I.Spec("m_bf16_q4_causal", 3, ("fixed", (1, 6, 300)), 4, 2, 2, 128, 16, "bf16", seed=31, causal=1),
+    I.Spec("m_bf16_q3_win", 3, ("fixed", (2, 70, 300)), 3, 1, 3, 128, 64, "bf16", seed=32, window=37),
+    I.Spec("m_fp8tok_q4_causal_win", 2, ("fixed", (257, 600)), 4, 1, 4, 256, 16, "fp8", "token", seed=33,
+           causal=1, window=100),
+    I.Spec("m_fp8_trans_q1_win", 2, ("fixed", (129, 513)), 1, 1, 8, 128, 128, "fp8", "tensor", "trans", seed=34,
+           window=256),
+    I.Spec("m_bf16_q2_causal_w1", 2, ("fixed", (1, 40)), 2, 1, 2, 128, 16, "bf16", seed=35, causal=1, window=1),
+]
+
+
+@pytest.mark.parametrize("spec", MASK_SPECS, ids=lambda s: s.name)
+def test_masked_oracle_equals_brute_force_dense(spec):
+    """Causal and windowed rows against dense attention with an explicit position mask."""
+    case = I.make_case(spec)
+    got = oracle.pa_decode(case)
+    want = dense_reference(case)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("spec", [MASK_SPECS[0], MASK_SPECS[2]], ids=lambda s: s.name)
+def test_causal_off_by_one_is_caught(spec):
+    case = I.make_case(spec)
+    got = oracle.pa_decode(case)
+    for shift in (-1, 1):
+        wrong = dense_reference(case, causal_shift=shift)
+        assert np.abs(got - wrong).max() > 1e-3
+
+
+def test_causal_row_equals_shorter_non_causal_decode():
+    """Row i of a causal decode over L tokens is the plain decode over the
+    first L - qlen + i + 1 tokens (same pages, same query row)."""
+    case = I.make_case(MASK_SPECS[0].replace(lens=("fixed", (9, 40, 300))), fill="zero")
+    got = oracle.pa_decode(case)
+    QL = case.qlen
+    for i in range(QL):
+        lens = (case.context_lens - QL + i + 1).clamp(min=0)
+        short = dataclasses.replace(case, context_lens=lens.to(torch.int32), causal=0)
+        want = oracle.pa_decode(short)
+        np.testing.assert_array_equal(got[:, i], want[:, i])
+
+
+def test_window_of_one_gives_the_last_v_row_exactly():
+    """A one-token window puts all weight on position e_i - 1: the output is that V row."""
+    spec = I.Spec("w1", 2, ("fixed", (5, 100)), 2, 1, 2, 128, 16, "bf16", seed=36, window=1, causal=1)
+    case = I.make_case(spec, fill="zero")
+    got = oracle.pa_decode(case)
+    for b in range(case.num_seqs):
+        L = int(case.context_lens[b])
+        for i in range(case.qlen):
+            t = L - case.qlen + i
+            page = int(case.block_tables[b, t // case.page_size])
+            for h in range(case.num_q_heads):
+                v = case.value_cache[page, h // case.q_per_kv, t % case.page_size].double().numpy()
+                np.testing.assert_array_equal(got[b, i, h], v)
+
+
+def test_window_at_least_the_context_is_no_window():
+    spec = MASK_SPECS[1].replace(window=300)
+    case = I.make_case(spec)
+    got = oracle.pa_decode(case)
+    plain = oracle.pa_decode(dataclasses.replace(case, window=0))
+    np.testing.assert_array_equal(got, plain)
+    tighter = oracle.pa_decode(dataclasses.replace(case, window=299))
+    assert np.abs(tighter[2] - got[2]).max() > 0  # L = 300: a 299-token window drops position 0
+
+
+def test_empty_causal_rows_are_zero():
+    """With L < qlen the first query tokens see no position: their rows are 0."""
+    case = I.make_case(MASK_SPECS[0])  # L = 1 with qlen 4
+    got = oracle.pa_decode(case)
+    assert np.all(got[0, :3] == 0) and np.any(got[0, 3] != 0)
