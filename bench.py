@@ -72,7 +72,8 @@ def kernel_tag_of(spec) -> str:
     vt = 1 if spec.v_layout == "trans" else 0
     nt = 1 if spec.qlen * spec.q_per_kv <= 16 else 2
     qf = 1 if spec.q_dtype == "fp8" else 0
-    return "Cfg<%d, %d, %d, %d, %d, %d, %d, 0>" % (kv, sc, vt, spec.head_dim, spec.page_size, nt, qf)
+    win = 1 if spec.window > 0 or (spec.causal and spec.qlen > 1) else 0
+    return "Cfg<%d, %d, %d, %d, %d, %d, %d, 0, %d>" % (kv, sc, vt, spec.head_dim, spec.page_size, nt, qf, win)
 
 
 def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
@@ -126,6 +127,19 @@ def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
         fh.write("\n")
     print("Calibration (1 GiB torch.neg copy): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f\n" % (f_factor, w_factor))
     print("\n".join(lines))
+
+
+def read_bytes(case) -> int:
+    """Algorithmic KV bytes of a call: K, V and scales of the tokens some query
+    row attends to. That is [max(0, e_0 - window), L) per sequence with a
+    window (e_0 = L - qlen + 1 when causal, else L), else all of [0, L)."""
+    if not getattr(case, "window", 0):
+        return case.kv_bytes()
+    toks = 0
+    for L in case.context_lens.tolist():
+        e0 = max(0, L - case.qlen + 1) if case.causal else L
+        toks += L - max(0, e0 - case.window)
+    return toks * case.num_kv_heads * case.kv_bytes_per_token_head()
 
 
 def time_cpu_oracle(case, target_s=15.0):
@@ -206,7 +220,7 @@ def time_all(steps, warmup):
         torch.cuda.synchronize()
         t_ms, m_ms, n = plan.read_timing()
         plan.set_timing(False)
-        nbytes = case.kv_bytes()
+        nbytes = read_bytes(case)
         inf = plan.info()
         gbps = nbytes / (us * 1e-6) / 1e9
         rows[spec.name] = {"us_per_call": round(us, 2), "tile_us": round(t_ms / n * 1e3, 2),

@@ -96,6 +96,18 @@ typedef enum pa_q_dtype { PA_Q_BF16 = 0, PA_Q_FP8_E4M3 = 1 } pa_q_dtype;
  *                       instruction sums some operand mixes to only about 2^-13
  *                       of their largest product, so near-tied logits can move
  *                       single output elements beyond 2e-2.
+ *   causal              0 (default): every query token attends to all of [0, L).
+ *                       1: the qlen query tokens are the last qlen positions of
+ *                       the sequence (their K/V already in the cache, as in
+ *                       multi-token verification); token i attends to
+ *                       t < e_i = L - qlen + i + 1 ([P1] "Tests": qlen 1-4
+ *                       probes; the causal select of the later tile commit).
+ *   window              0 (default): no sliding window. W > 0: token i attends
+ *                       only to t >= e_i - W as well (the W positions ending at
+ *                       its own). Tiles and block-table columns wholly before
+ *                       every row's window are never read. A row whose range is
+ *                       empty is written as 0. Not offered with MXFP4 ([P2]
+ *                       "Summary": sliding window is refused there).
  */
 typedef struct pa_problem {
     int32_t num_seqs;
@@ -115,6 +127,8 @@ typedef struct pa_problem {
     int32_t max_partitions;
     int32_t task_budget;
     int32_t mxfp4_scaled_qk;
+    int32_t causal;
+    int32_t window;
 } pa_problem;
 
 /* Opaque plan: validated problem, task list and partition workspace. */

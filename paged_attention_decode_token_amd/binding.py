@@ -39,7 +39,7 @@ class pa_problem(ctypes.Structure):
         "num_seqs", "qlen", "num_kv_heads", "q_per_kv", "head_dim", "page_size", "num_blocks",
         "max_blocks_per_seq", "max_context_len", "kv_dtype", "scale_mode", "v_layout", "q_dtype")] + [
         ("softmax_scale", ctypes.c_float), ("max_partitions", ctypes.c_int32), ("task_budget", ctypes.c_int32),
-        ("mxfp4_scaled_qk", ctypes.c_int32)]
+        ("mxfp4_scaled_qk", ctypes.c_int32), ("causal", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 class pa_plan_info(ctypes.Structure):
@@ -104,11 +104,12 @@ def _check(st: int):
 
 def make_problem(num_seqs, qlen, num_kv_heads, q_per_kv, head_dim, page_size, num_blocks, max_blocks_per_seq,
                  max_context_len, kv_dtype="bf16", scale_mode="none", v_layout="plain", q_dtype="bf16",
-                 softmax_scale=0.0, max_partitions=0, task_budget=0, mxfp4_scaled_qk=0) -> pa_problem:
+                 softmax_scale=0.0, max_partitions=0, task_budget=0, mxfp4_scaled_qk=0, causal=0,
+                 window=0) -> pa_problem:
     return pa_problem(num_seqs, qlen, num_kv_heads, q_per_kv, head_dim, page_size, num_blocks, max_blocks_per_seq,
                       max_context_len, KV_DTYPES.get(kv_dtype, kv_dtype), SCALE_MODES.get(scale_mode, scale_mode),
                       V_LAYOUTS.get(v_layout, v_layout), Q_DTYPES.get(q_dtype, q_dtype), float(softmax_scale),
-                      max_partitions, task_budget, int(mxfp4_scaled_qk))
+                      max_partitions, task_budget, int(mxfp4_scaled_qk), int(causal), int(window))
 
 
 def problem_of(case, **over) -> pa_problem:
@@ -117,7 +118,8 @@ def problem_of(case, **over) -> pa_problem:
               head_dim=case.head_dim, page_size=case.page_size, num_blocks=case.num_blocks,
               max_blocks_per_seq=case.max_blocks_per_seq, max_context_len=case.max_context_len,
               kv_dtype=case.kv_dtype, scale_mode=case.scale_mode, v_layout=case.v_layout, q_dtype=case.q_dtype,
-              softmax_scale=case.softmax_scale or 0.0)
+              softmax_scale=case.softmax_scale or 0.0, causal=getattr(case, "causal", 0),
+              window=getattr(case, "window", 0))
     kw.update(over)
     return make_problem(**kw)
 

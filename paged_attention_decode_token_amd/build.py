@@ -31,11 +31,16 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    srcs = [os.path.join(CSRC, "pa_kernels.hip"), os.path.join(CSRC, "pa_api.cpp")]
-    objs = [os.path.join(bdir, os.path.basename(s) + ".o") for s in srcs]
+    # the kernel instances are compiled in four shards (see the dispatch section
+    # of pa_kernels.hip), in parallel with the host code
+    kern = os.path.join(CSRC, "pa_kernels.hip")
+    jobs = [(kern, os.path.join(bdir, "pa_kernels.%d.o" % i), ["-DPA_SHARD=%d" % i]) for i in range(4)]
+    jobs.append((os.path.join(CSRC, "pa_api.cpp"), os.path.join(bdir, "pa_api.cpp.o"), []))
+    objs = [j[1] for j in jobs]
 
-    def compile_one(src, obj):
-        cmd = [hipcc, *flags(), "-x", "hip", "-c", src, "-o", obj]
+    def compile_one(job):
+        src, obj, defs = job
+        cmd = [hipcc, *flags(), *defs, "-x", "hip", "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = r.stdout + "".join(l + "\n" for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
         if r.returncode != 0:
@@ -43,8 +48,8 @@ def build(verbose: bool = False) -> str:
         if verbose and out.strip():
             print(out, file=sys.stderr)
 
-    with cf.ThreadPoolExecutor(max_workers=2) as ex:
-        list(ex.map(compile_one, srcs, objs))
+    with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        list(ex.map(compile_one, jobs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

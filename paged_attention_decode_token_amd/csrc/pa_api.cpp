@@ -91,6 +91,8 @@ pa_status validate(const pa_problem* p) {
     if (!(std::isfinite(p->softmax_scale))) return fail(PA_ERR_INVALID_ARG, "softmax_scale is not finite");
     if (p->mxfp4_scaled_qk != 0 && p->mxfp4_scaled_qk != 1)
         return fail(PA_ERR_INVALID_ARG, "mxfp4_scaled_qk must be 0 or 1");
+    if (p->causal != 0 && p->causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (p->window < 0) return fail(PA_ERR_INVALID_ARG, "window must be >= 0");
     if (p->max_partitions < 0 || p->task_budget < 0)
         return fail(PA_ERR_INVALID_ARG, "max_partitions and task_budget must be >= 0");
     if (p->max_partitions > 64) return fail(PA_ERR_UNSUPPORTED, "max_partitions %d (supported: <= 64)", p->max_partitions);
@@ -119,6 +121,7 @@ pa_status validate(const pa_problem* p) {
         if (p->qlen != 1) return fail(PA_ERR_UNSUPPORTED, "MXFP4 needs qlen 1");
         if (p->q_per_kv > 16) return fail(PA_ERR_UNSUPPORTED, "MXFP4 supports up to 16 query heads per KV head");
         if (p->v_layout != PA_V_PLAIN) return fail(PA_ERR_UNSUPPORTED, "MXFP4 needs the plain V layout");
+        if (p->window != 0) return fail(PA_ERR_UNSUPPORTED, "MXFP4 has no sliding window");
     }
     return PA_OK;
 }
@@ -133,6 +136,7 @@ pa::KernelKey key_of(const pa_problem& p) {
     k.ntiles_n = rows_of(p) <= 16 ? 1 : 2;
     k.q_fp8 = p.q_dtype == PA_Q_FP8_E4M3 ? 1 : 0;
     k.mx_scaled = (p.kv_dtype == PA_KV_MXFP4 && p.mxfp4_scaled_qk) ? 1 : 0;
+    k.win = (p.window > 0 || (p.causal && p.qlen > 1)) ? 1 : 0;  // qlen 1: causal is the plain decode
     return k;
 }
 
@@ -222,7 +226,7 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int 
     const int max_parts = p.max_partitions > 0 ? p.max_partitions : 64;
     const int slots = std::max(1, num_cus * std::max(1, blocks_per_cu));
     const long cap_tokens = (long)p.max_blocks_per_seq * p.page_size;
-    std::vector<int> tiles(B);
+    std::vector<int> tiles(B), first(B, 0);  // tiles to read per sequence, from tile first[b] on
     for (int b = 0; b < B; ++b) {
         long L = lens ? lens[b] : p.max_context_len;
         if (lens) {
@@ -237,6 +241,13 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int 
             L = std::min(L, cap_tokens);
         }
         tiles[b] = (int)((L + pa::kTileTokens - 1) / pa::kTileTokens);
+        if (lens && p.window > 0) {
+            // tiles before the first query token's window are never read
+            const long e0 = p.causal ? L - p.qlen + 1 : L;
+            const long s0 = std::max(0L, e0 - p.window);
+            first[b] = (int)std::min<long>(s0 / pa::kTileTokens, tiles[b]);
+            tiles[b] -= first[b];
+        }
     }
     long work = 0;
     int tmax = 0;
@@ -283,7 +294,7 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int 
         for (int kvh = 0; kvh < H; ++kvh)
             for (int part = 0; part < P; ++part) {
                 const int t0 = (int)((long)part * tiles[b] / P), t1 = (int)((long)(part + 1) * tiles[b] / P);
-                out->tasks.insert(out->tasks.end(), {b, kvh | (part << 16), t0, t1});
+                out->tasks.insert(out->tasks.end(), {b, kvh | (part << 16), first[b] + t0, first[b] + t1});
             }
     }
     // longest first; ties keep (sequence, head, partition) order
@@ -485,6 +496,8 @@ pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_ca
     a.num_blocks = p.num_blocks;
     const double sm = p.softmax_scale != 0.f ? (double)p.softmax_scale : 1.0 / std::sqrt((double)p.head_dim);
     a.scale_log2 = (float)(sm * 1.4426950408889634);
+    a.causal = p.causal;
+    a.window = p.window;
     a.plan_free = 0;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -548,6 +561,8 @@ pa_status pa_decode_direct(const pa_problem* problem, const void* query, const v
     a.num_blocks = p.num_blocks;
     const double sm = p.softmax_scale != 0.f ? (double)p.softmax_scale : 1.0 / std::sqrt((double)p.head_dim);
     a.scale_log2 = (float)(sm * 1.4426950408889634);
+    a.causal = p.causal;
+    a.window = p.window;
     a.plan_free = 1;
     e = pa::launch_tile(key, a, p.num_seqs * p.num_kv_heads, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "tile kernel launch failed: %s", hipGetErrorString(e));

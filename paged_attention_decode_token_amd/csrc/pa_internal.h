@@ -33,10 +33,13 @@ struct TileArgs {
     int32_t num_seqs, qlen, num_kv_heads, q_per_kv, rows, max_blocks, num_blocks;
     float scale_log2;  // softmax_scale * log2(e)
     int32_t plan_free;  // 1: one task per (sequence, KV head) from the block index, tasks unused
+    int32_t causal;     // 1: query token i attends to t < L - qlen + i + 1
+    int32_t window;     // > 0: and to t >= (that end) - window
 };
 
 struct KernelKey {
     int kv, scale, vt, head_dim, page, ntiles_n, q_fp8, mx_scaled;
+    int win;  // causal rows (qlen > 1) or a sliding window
 };
 
 // Launch the tile kernel for `key` (returns hipErrorInvalidValue for a key with

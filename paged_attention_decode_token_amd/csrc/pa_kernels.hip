@@ -153,10 +153,18 @@ PA_DEV uint32_t keep_bytes(int valid) {
     return valid >= 4 ? 0xFFFFFFFFu : ((1u << (8 * valid)) - 1u);
 }
 
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 // ----------------------------------------------------------- configuration
 
-template <int KV_, int SC_, int VT_, int D_, int PG_, int NT_, int QF8_, int MXS_>
+template <int KV_, int SC_, int VT_, int D_, int PG_, int NT_, int QF8_, int MXS_, int WIN_>
 struct Cfg {
+    // causal rows or a sliding window: masked tiles may also open the range
+    // (the window's first tiles) and close it before the context boundary
+    static constexpr bool WIN = WIN_ != 0;
     static constexpr int KV = KV_;
     static constexpr int SC = SC_;
     static constexpr bool VT = VT_ != 0;
@@ -241,6 +249,7 @@ struct State {
 
 struct Ctx {
     int b, kvh, L, npages, lane, ln, lg, wave;
+    int row_s[2], row_e[2];  // token range [row_s, row_e) of this lane's query row in N tile 0 / 1
     const int32_t* bt_row;
     const char* kbase;   // K data of this head in page 0
     const char* vbase;   // V data of this head in page 0
@@ -607,7 +616,9 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
                 const int t = 16 * lg + 4 * c + j;
                 float x = acc[c][nt][j] * sc;
                 if constexpr (C::SC == SC_TOKEN) x *= kb.tks[4 * c + j];
-                if (MASK) x = (cb + t < cx.L) ? x : -__builtin_inff();  // select, never a multiply
+                // outside the row's causal / window range, or at or past L: -inf by a
+                // select, never a multiply
+                if (MASK) x = (cb + t >= cx.row_s[nt] && cb + t < cx.row_e[nt]) ? x : -__builtin_inff();
                 acc[c][nt][j] = x;
                 mloc = fmaxf(mloc, x);
             }
@@ -731,45 +742,74 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
             }
             wave_lds_sync();  // staged rows are read back by other lanes of the same wave
         }
+        if constexpr (C::VDMA) {
+            // The transposed reads of four d tiles are issued together, then
+            // widened and multiplied, so that LDS latency overlaps the MFMAs.
+            constexpr int CH = 4;
+            typedef int i32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int d0 = 0; d0 < C::DT; d0 += CH) {
+                u32x4 raw[CH];
+#pragma unroll
+                for (int k = 0; k < CH; ++k) {
+                    const int dt = d0 + k;
+                    if constexpr (C::KV == KV_BF16) {
+                        // A lane (m, g) needs V[16g + 8s + e][16dt + m], e in [0, 8):
+                        // two transposed reads; source lane ln reads row
+                        // 16g + 8s + (ln >> 2) (+ 4), columns 16dt + 4 (ln & 3) + [0, 4)
+                        const int r0 = 16 * lg + 8 * s + (ln >> 2);
+                        const int c = 2 * dt + ((ln & 3) >> 1);
+                        // vswz is the same for r0 and r0 + 4
+                        const char* base = vlds + r0 * C::ROWB + 16 * (c ^ vswz<C>(r0)) + 8 * (ln & 1);
+                        bf16x4 r0v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (__attribute__((address_space(3))) bf16x4*)(base));
+                        bf16x4 r1v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (__attribute__((address_space(3))) bf16x4*)(base + 4 * C::ROWB));
+                        raw[k] = __builtin_bit_cast(u32x4, bf16x8{r0v[0], r0v[1], r0v[2], r0v[3], r1v[0], r1v[1],
+                                                                  r1v[2], r1v[3]});
+                    } else {
+                        // e4m3: one transposed byte read gives lane (m, g) the 8 bytes
+                        // V[16g + 8s + e][16dt + m]; source lane ln reads 8 bytes of
+                        // row 16g + 8s + (ln >> 1) at column 16dt + 8 (ln & 1)
+                        const int r = 16 * lg + 8 * s + (ln >> 1);
+                        const char* base = vlds + r * C::ROWB + 16 * (dt ^ vswz<C>(r)) + 8 * (ln & 1);
+                        i32x2 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(base));
+                        raw[k] = u32x4{(uint32_t)b[0], (uint32_t)b[1], 0u, 0u};
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < CH; ++k) {
+                    const int dt = d0 + k;
+                    // element / byte e of this lane is token cb + 16g + 8s + e: zero
+                    // those at or past L (PR #7092, "Fix")
+                    const int valid = cx.L - (cb + 16 * lg + 8 * s);
+                    bf16x8 va;
+                    if constexpr (C::KV == KV_BF16) {
+                        u32x4 w = raw[k];
+                        if (MASK) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                w[j] &= (valid > 2 * j ? 0x0000FFFFu : 0u) | (valid > 2 * j + 1 ? 0xFFFF0000u : 0u);
+                        }
+                        va = as_bf16x8(w);
+                    } else {
+                        uint32_t b0 = raw[k][0], b1 = raw[k][1];
+                        if (MASK) {
+                            b0 &= keep_bytes(valid);
+                            b1 &= keep_bytes(valid - 4);
+                        }
+                        va = fp8x8_to_bf16x8(b0, b1);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pf.hi[s][nt]), st.o[dt][nt]);
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
             bf16x8 va;
-            if constexpr (C::VDMA && C::KV == KV_BF16) {
-                // A lane (m, g) needs V[16g + 8s + e][16dt + m], e in [0, 8): two
-                // transposed reads; source lane ln reads row 16g + 8s + (ln >> 2)
-                // (+ 4), columns 16dt + 4 (ln & 3) + [0, 4)
-                const int r0 = 16 * lg + 8 * s + (ln >> 2);
-                const int c = 2 * dt + ((ln & 3) >> 1);
-                const char* base = vlds + r0 * C::ROWB + 16 * (c ^ vswz<C>(r0)) + 8 * (ln & 1);
-                // vswz is the same for r0 and r0 + 4
-                bf16x4 r0v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base));
-                bf16x4 r1v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (__attribute__((address_space(3))) bf16x4*)(base + 4 * C::ROWB));
-                u32x4 w = __builtin_bit_cast(u32x4, bf16x8{r0v[0], r0v[1], r0v[2], r0v[3], r1v[0], r1v[1], r1v[2], r1v[3]});
-                if (MASK) {
-                    // element e is token cb + 16g + 8s + e: zero those at or past L (PR #7092, "Fix")
-                    const int valid = cx.L - (cb + 16 * lg + 8 * s);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        w[j] &= (valid > 2 * j ? 0x0000FFFFu : 0u) | (valid > 2 * j + 1 ? 0xFFFF0000u : 0u);
-                }
-                va = as_bf16x8(w);
-            } else if constexpr (C::VDMA) {
-                // e4m3: one transposed byte read gives lane (m, g) the 8 bytes
-                // V[16g + 8s + e][16dt + m]; source lane ln reads 8 bytes of row
-                // 16g + 8s + (ln >> 1) at column 16dt + 8 (ln & 1)
-                const int r = 16 * lg + 8 * s + (ln >> 1);
-                const char* base = vlds + r * C::ROWB + 16 * (dt ^ vswz<C>(r)) + 8 * (ln & 1);
-                typedef int i32x2 __attribute__((ext_vector_type(2)));
-                i32x2 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(base));
-                uint32_t b0 = (uint32_t)b[0], b1 = (uint32_t)b[1];
-                if (MASK) {
-                    const int valid = cx.L - (cb + 16 * lg + 8 * s);  // byte e is token cb + 16g + 8s + e
-                    b0 &= keep_bytes(valid);
-                    b1 &= keep_bytes(valid - 4);
-                }
-                va = fp8x8_to_bf16x8(b0, b1);
-            } else if constexpr (C::STAGE_V) {
+            if constexpr (C::STAGE_V) {
                 // A lane (m = d offset, g) needs rows 8g + [0, 8) at column 16dt + m
                 const char* base = vlds + (8 * lg + (ln >> 2)) * C::VPITCH + 2 * (16 * dt + 4 * (ln & 3));
                 bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -862,36 +902,69 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     }
 
     char* vlds = smem + cx.wave * C::VSTAGE_BYTES;
-    // Tiles [tb, te_full) are full (every token owned); tile te - 1 is the
-    // boundary tile when te > te_full. Loads run one stage ahead: V(j) is
-    // issued at the top of iteration j (right after PV(j - 1)), K(j + 1) right
-    // after QK(j). Every load of the loop is unconditional and the loop test
-    // comes after PV, so the waits before QK and PV cover exactly the loads
-    // of the current slice, never the prefetch in flight. The last tile of
-    // the task runs after the loop with its own V loads, masked (a no-op on a
-    // full tile).
-    const int te_full = max(tb, min(te, L / kTileTokens));
-    const int nfull = te_full - tb;
-    const bool has_bnd = te > te_full;
-    const int total = nfull + (has_bnd ? 1 : 0);
-    if (total > 0) {
-        int cb = tb * kTileTokens + 64 * cx.wave;
+
+    // Query row r of this lane (query token i = r / G) attends to
+    // [row_s, row_e): e = L - qlen + i + 1 when causal, else L; s = e - window
+    // with a sliding window, else 0.
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        if constexpr (C::WIN) {
+            const int r = 16 * nt + cx.ln;
+            const int i = r < a.rows ? r / a.q_per_kv : a.qlen - 1;
+            const int e = a.causal ? L - a.qlen + i + 1 : L;
+            cx.row_e[nt] = e;
+            cx.row_s[nt] = a.window > 0 ? e - a.window : 0;
+        } else {
+            cx.row_e[nt] = L;
+            cx.row_s[nt] = 0;
+        }
+    }
+    // Tiles of the task: [T0, T1), the task's range cut to the tiles any row
+    // reads (from the first row's window start to ceil(L / 256)). Tiles
+    // [F0, F1) lie inside every row's range and run unmasked; the others
+    // (the window's first tiles, the causal and context boundary at the end)
+    // run the masked variant. Loads run one stage ahead: V(j) is issued at
+    // the top of iteration j (right after PV(j - 1)), K(j + 1) right after
+    // QK(j). Every load of a loop is unconditional and each loop test comes
+    // after PV, so the waits before QK and PV cover exactly the loads of the
+    // current slice, never the prefetch in flight. The last tile runs after
+    // the loops with its own V loads, masked (a no-op on a full tile).
+    const int e_min = C::WIN ? max(0, a.causal ? L - a.qlen + 1 : L) : L;  // smallest row end
+    const int s_min = C::WIN && a.window > 0 ? max(0, e_min - a.window) : 0;
+    const int s_max = C::WIN && a.window > 0 ? max(0, L - a.window) : 0;
+    const int T0 = max(tb, s_min / kTileTokens);
+    const int T1 = te;
+    const int F0 = max(T0, (s_max + kTileTokens - 1) / kTileTokens);
+    const int F1 = max(F0, min(T1, e_min / kTileTokens));
+    if (T1 > T0) {
+        int cb = T0 * kTileTokens + 64 * cx.wave;
         PageCache<C> pc;
-        page_cache_fill<C>(a, cx, pc, tb);
-        SlicePages<C> sp = slice_pages<C>(a, cx, pc, tb);
+        page_cache_fill<C>(a, cx, pc, T0);
+        SlicePages<C> sp = slice_pages<C>(a, cx, pc, T0);
         KBuf<C> kb;
         VBuf<C> vb;
         load_k<C>(a, cx, sp, kb);
-        for (int j = 0; j + 1 < total; ++j) {  // full tiles followed by another tile
+        int tile = T0;
+        // one tile with a successor: V(tile), QK, K(tile + 1), PV
+        auto step = [&](auto mask_tag) {
+            constexpr bool M = decltype(mask_tag)::value;
             dma_fence<C>();
             load_v<C>(a, cx, sp, vb, vlds);
             PFrag<C> pf;
-            qk_softmax<C, false>(a, cx, qf, kb, st, pf, cb);
-            sp = slice_pages<C>(a, cx, pc, tb + j + 1);
+            qk_softmax<C, M>(a, cx, qf, kb, st, pf, cb);
+            sp = slice_pages<C>(a, cx, pc, tile + 1);
             load_k<C>(a, cx, sp, kb);
-            pv<C, false, C::KVMEM>(cx, vb, pf, st, cb, vlds);
+            pv<C, M, C::KVMEM>(cx, vb, pf, st, cb, vlds);
             cb += kTileTokens;
-        }
+            ++tile;
+        };
+        using Masked = BoolTag<true>;
+        using Full = BoolTag<false>;
+        if constexpr (C::WIN)
+            for (; tile < F0 && tile + 1 < T1;) step(Masked{});  // window head
+        for (; tile < F1 && tile + 1 < T1;) step(Full{});        // the bulk
+        if constexpr (C::WIN)
+            for (; tile + 1 < T1;) step(Masked{});               // causal boundary
         dma_fence<C>();
         load_v<C>(a, cx, sp, vb, vlds);
         PFrag<C> pf;
@@ -1082,30 +1155,63 @@ struct Entry {
     TileFn fn;
 };
 
-#define PA_E(KV, SC, VT, D, PG, NT, QF) PA_EM(KV, SC, VT, D, PG, NT, QF, 0)
-#define PA_EM(KV, SC, VT, D, PG, NT, QF, MXS) \
-    {{KV, SC, VT, D, PG, NT, QF, MXS}, &pa_tile_kernel<Cfg<KV, SC, VT, D, PG, NT, QF, MXS>>}
-#define PA_PG(KV, SC, VT, D, NT) PA_E(KV, SC, VT, D, 16, NT, 0), PA_E(KV, SC, VT, D, 64, NT, 0), PA_E(KV, SC, VT, D, 128, NT, 0)
-#define PA_NT(KV, SC, VT, D) PA_PG(KV, SC, VT, D, 1), PA_PG(KV, SC, VT, D, 2)
-#define PA_D(KV, SC, VT) PA_NT(KV, SC, VT, 128), PA_NT(KV, SC, VT, 256)
-#define PA_VT(KV, SC) PA_D(KV, SC, 0), PA_D(KV, SC, 1)
+// Kernel instances are compiled in shards (PA_SHARD 0..3, one object file
+// each, built in parallel); without PA_SHARD one object holds them all.
+//   0: bf16 and MXFP4, plain decode      1: bf16 with causal rows / a window
+//   2: e4m3 caches, plain decode         3: e4m3 with causal rows / a window
+// Shard 0 also holds the merge kernel and the dispatch functions.
+#ifndef PA_SHARD
+#define PA_SHARD -1
+#endif
+#define PA_IN_SHARD(n) (PA_SHARD == -1 || PA_SHARD == (n))
 
-static const Entry kEntries[] = {
-    PA_VT(KV_BF16, SC_NONE),
-    PA_VT(KV_FP8, SC_TENSOR),
-    PA_VT(KV_FP8, SC_TOKEN),
-    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 0, 0),
-    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 1, 0),
-    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 0, 1),
-    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 1, 1),
+#define PA_E(KV, SC, VT, D, PG, NT, QF, W) PA_EM(KV, SC, VT, D, PG, NT, QF, 0, W)
+#define PA_EM(KV, SC, VT, D, PG, NT, QF, MXS, W) \
+    {{KV, SC, VT, D, PG, NT, QF, MXS, W}, &pa_tile_kernel<Cfg<KV, SC, VT, D, PG, NT, QF, MXS, W>>}
+#define PA_PG(KV, SC, VT, D, NT, W) \
+    PA_E(KV, SC, VT, D, 16, NT, 0, W), PA_E(KV, SC, VT, D, 64, NT, 0, W), PA_E(KV, SC, VT, D, 128, NT, 0, W)
+#define PA_NT(KV, SC, VT, D, W) PA_PG(KV, SC, VT, D, 1, W), PA_PG(KV, SC, VT, D, 2, W)
+#define PA_D(KV, SC, VT, W) PA_NT(KV, SC, VT, 128, W), PA_NT(KV, SC, VT, 256, W)
+#define PA_VT(KV, SC, W) PA_D(KV, SC, 0, W), PA_D(KV, SC, 1, W)
+
+#if PA_IN_SHARD(0)
+extern const Entry kShard0[] = {
+    PA_VT(KV_BF16, SC_NONE, 0),
+    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 0, 0, 0),
+    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 1, 0, 0),
+    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 0, 1, 0),
+    PA_EM(KV_MXFP4, SC_NONE, 0, 128, 128, 1, 1, 1, 0),
 };
+extern const int kShard0Size = sizeof(kShard0) / sizeof(kShard0[0]);
+#endif
+#if PA_IN_SHARD(1)
+extern const Entry kShard1[] = {PA_VT(KV_BF16, SC_NONE, 1)};
+extern const int kShard1Size = sizeof(kShard1) / sizeof(kShard1[0]);
+#endif
+#if PA_IN_SHARD(2)
+extern const Entry kShard2[] = {PA_VT(KV_FP8, SC_TENSOR, 0), PA_VT(KV_FP8, SC_TOKEN, 0)};
+extern const int kShard2Size = sizeof(kShard2) / sizeof(kShard2[0]);
+#endif
+#if PA_IN_SHARD(3)
+extern const Entry kShard3[] = {PA_VT(KV_FP8, SC_TENSOR, 1), PA_VT(KV_FP8, SC_TOKEN, 1)};
+extern const int kShard3Size = sizeof(kShard3) / sizeof(kShard3[0]);
+#endif
+
+#if PA_IN_SHARD(0)
+extern const Entry kShard1[], kShard2[], kShard3[];
+extern const int kShard1Size, kShard2Size, kShard3Size;
 
 static TileFn find(const KernelKey& k) {
-    for (const Entry& e : kEntries)
-        if (e.key.kv == k.kv && e.key.scale == k.scale && e.key.vt == k.vt && e.key.head_dim == k.head_dim &&
-            e.key.page == k.page && e.key.ntiles_n == k.ntiles_n && e.key.q_fp8 == k.q_fp8 &&
-            e.key.mx_scaled == k.mx_scaled)
-            return e.fn;
+    const Entry* tables[4] = {kShard0, kShard1, kShard2, kShard3};
+    const int sizes[4] = {kShard0Size, kShard1Size, kShard2Size, kShard3Size};
+    for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < sizes[t]; ++i) {
+            const Entry& e = tables[t][i];
+            if (e.key.kv == k.kv && e.key.scale == k.scale && e.key.vt == k.vt && e.key.head_dim == k.head_dim &&
+                e.key.page == k.page && e.key.ntiles_n == k.ntiles_n && e.key.q_fp8 == k.q_fp8 &&
+                e.key.mx_scaled == k.mx_scaled && e.key.win == k.win)
+                return e.fn;
+        }
     return nullptr;
 }
 
@@ -1139,5 +1245,6 @@ hipError_t launch_merge(const TileArgs& args, int head_dim, hipStream_t stream) 
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
+#endif  // PA_IN_SHARD(0)
 
 }  // namespace pa

@@ -134,8 +134,13 @@ MXFP4_SHORT_QBF = MXFP4_SHORT_Q8.replace(name="mxfp4_p128_b16_l2048_qbf16", q_dt
 MXFP4_LONG_Q8 = MXFP4_SHORT_Q8.replace(name="mxfp4_p128_b16_l131072_qfp8", lens=("const", 131072), seed=1008)
 MXFP4_LONG_QBF = MXFP4_LONG_Q8.replace(name="mxfp4_p128_b16_l131072_qbf16", q_dtype="bf16", seed=1009)
 
+# Masked variants: a 1024-token sliding window on the bf16 batch, and causal
+# multi-token verification (qlen 4) on the fp8 per-token batch.
+BF16_P64_W1024 = BF16_P64.replace(name="bf16_p64_b64_w1024", window=1024, seed=1010)
+FP8TOK_Q4_CAUSAL = FP8TOK_Q4.replace(name="fp8tok_p16_b16_q4_causal", causal=1, seed=1011)
+
 FULL = [TINY_BF16, BF16_P64, BF16_P128, FP8TOK_Q1, FP8TOK_Q4, FP8_TRANS, MXFP4_SHORT_Q8, MXFP4_SHORT_QBF,
-        MXFP4_LONG_Q8, MXFP4_LONG_QBF]
+        MXFP4_LONG_Q8, MXFP4_LONG_QBF, BF16_P64_W1024, FP8TOK_Q4_CAUSAL]
 BY_NAME = {s.name: s for s in FULL}
 
 

@@ -53,6 +53,9 @@ def _prob(**kw):
     (dict(kv_dtype="mxfp4", page_size=128, v_layout="trans"), B.PA_ERR_UNSUPPORTED),
     (dict(q_dtype="fp8"), B.PA_ERR_UNSUPPORTED),  # e4m3 query only with MXFP4
     (dict(softmax_scale=float("nan")), B.PA_ERR_INVALID_ARG),
+    (dict(causal=2), B.PA_ERR_INVALID_ARG),
+    (dict(window=-1), B.PA_ERR_INVALID_ARG),
+    (dict(kv_dtype="mxfp4", page_size=128, window=64), B.PA_ERR_UNSUPPORTED),
 ])
 def test_refusals(kw, status):
     with pytest.raises(B.PaError) as ei:
@@ -140,3 +143,23 @@ def test_full_workload_plans():
                            width, max(case_lens), spec.kv_dtype, spec.scale_mode, spec.v_layout, spec.q_dtype)
         tasks, parts, info = B.pa_plan_host(p, case_lens, num_cus=256)
         assert info.num_tasks >= 1 and info.max_parts <= 64
+
+
+@pytest.mark.parametrize("window,causal", [(300, 0), (1000, 1), (1, 1)])
+def test_planner_skips_tiles_before_the_window(window, causal):
+    """With host lengths, tasks start at the first tile of the first query
+    token's window and still cover every tile from there to ceil(L / 256)."""
+    lens = [0, 5, 255, 256, 700, 5000]
+    prob = _prob(num_seqs=len(lens), qlen=4, q_per_kv=4, max_blocks_per_seq=400, max_context_len=6000,
+                 causal=causal, window=window)
+    for budget in (0, 50, 100000):
+        prob.task_budget = budget
+        tasks, parts, info = B.pa_plan_host(prob, lens)
+        for b, L in enumerate(lens):
+            e0 = L - 4 + 1 if causal else L
+            first = max(0, e0 - window) // 256
+            ntiles = (L + 255) // 256
+            for kvh in range(prob.num_kv_heads):
+                mine = sorted((t[2], t[3]) for t in tasks.tolist() if t[0] == b and (t[1] & 0xFFFF) == kvh)
+                covered = [x for t0, t1 in mine for x in range(t0, t1)]
+                assert covered == list(range(min(first, ntiles), ntiles)), (b, L, mine)

@@ -224,3 +224,47 @@ def test_plan_free_full_size(spec):
     check_parity(out, oracle.pa_decode(case, seqs=seqs), seqs=seqs, what=spec.name + " plan-free (sampled)")
     planned, _ = run(case, max_partitions=1)
     assert torch.equal(out.view(torch.int16), planned.view(torch.int16))
+
+
+# ------------------------------------------------ causal and sliding window
+
+GPU_MASK_SPECS = [
+    I.Spec("g_bf16_q4_causal", 4, ("fixed", (1, 6, 300, 1030)), 4, 2, 2, 128, 16, "bf16", seed=41, causal=1),
+    I.Spec("g_bf16_q2_win", 4, ("fixed", (2, 70, 700, 1500)), 2, 1, 4, 128, 64, "bf16", seed=42, window=300),
+    I.Spec("g_fp8tok_q4_causal_win", 3, ("fixed", (257, 600, 1400)), 4, 1, 4, 256, 16, "fp8", "token", seed=43,
+           causal=1, window=500),
+    I.Spec("g_fp8trans_win", 3, ("fixed", (129, 513, 2000)), 1, 1, 8, 128, 128, "fp8", "tensor", "trans", seed=44,
+           window=700),
+    I.Spec("g_bf16_q2_causal_w1", 2, ("fixed", (1, 40)), 2, 1, 2, 128, 16, "bf16", seed=45, causal=1, window=1),
+    I.Spec("g_bf16_p128_w256", 3, ("fixed", (255, 256, 2049)), 1, 2, 8, 128, 128, "bf16", seed=46, window=256),
+    I.Spec("g_bf16_q4_g8_causal_win", 3, ("fixed", (3, 511, 1300)), 4, 1, 8, 128, 64, "bf16", seed=47, causal=1,
+           window=257),
+]
+
+
+@pytest.mark.parametrize("spec", GPU_MASK_SPECS, ids=lambda s: s.name)
+def test_masked_rows_agree_with_oracle(spec):
+    """Causal and windowed rows, planned (automatic and split into many
+    partitions) and plan-free, against the oracle; poison bit-identity."""
+    case = I.make_case(spec)
+    ref = oracle.pa_decode(case)
+    out, _ = run(case)
+    check_parity(out, ref, what=spec.name)
+    many, _ = run(case, task_budget=100000)
+    check_parity(many, ref, what=spec.name + " many partitions")
+    direct = run_direct(case)
+    check_parity(direct, ref, what=spec.name + " plan-free")
+    one, _ = run(case, max_partitions=1)
+    assert torch.equal(direct.view(torch.int16), one.view(torch.int16))
+    zero = run(I.refill(case, "zero"))[0]
+    assert torch.equal(zero.view(torch.int16), out.view(torch.int16))
+    # rows whose range is empty (causal with L < qlen) are written as zeros
+    ref_zero = np.all(ref == 0, axis=-1)
+    assert torch.all(out.float().cpu()[torch.from_numpy(ref_zero)] == 0)
+
+
+def test_mxfp4_refuses_a_window():
+    case = I.make_case(I.small(I.MXFP4_SHORT_QBF))
+    with pytest.raises(B.PaError) as ei:
+        B.pa_plan(B.problem_of(case, window=128), case.context_lens)
+    assert ei.value.status == B.PA_ERR_UNSUPPORTED
