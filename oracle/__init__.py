@@ -11,7 +11,8 @@ CPU arrays in, fp64 numpy arrays out.
 Parity pins (tests/test_oracle_*.py, all CPU): brute-force dense attention on
 tiny inputs, softmax normalisation, context_len = 1, all-equal and dominant
 keys, split/merge (log-sum-exp) invariance, page-permutation invariance, GQA
-grouping, and the format decoders against torch's own casts.
+grouping, the format decoders against torch's own casts, and the MXFP4 encoder
+against a hand-derived rounding table, exact round trips and its scale range.
 """
 from __future__ import annotations
 
@@ -90,6 +91,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
         L.oracle_f64_to_e4m3_rne_sat.restype = ctypes.c_uint8
         L.oracle_f64_to_e4m3_rne_sat.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_e2m1_rne_sat.restype = ctypes.c_uint8
+        L.oracle_f64_to_e2m1_rne_sat.argtypes = [ctypes.c_double]
+        L.oracle_mxfp4_encode_block.restype = None
+        L.oracle_mxfp4_encode_block.argtypes = [vp, vp, vp]
+        L.oracle_write_kv_mxfp4.restype = ctypes.c_int
+        L.oracle_write_kv_mxfp4.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_q_row_exponent.restype = ctypes.c_int
         L.oracle_q_row_exponent.argtypes = [ctypes.c_double]
         L.oracle_num_threads.restype = ctypes.c_int
@@ -178,6 +185,42 @@ def f64_to_bf16(x):
 
 def f64_to_e4m3(x):
     return lib().oracle_f64_to_e4m3_rne_sat(float(x))
+
+
+def f64_to_e2m1(x):
+    return lib().oracle_f64_to_e2m1_rne_sat(float(x))
+
+
+def mxfp4_encode_block(values):
+    """One 32-element block to MXFP4: (data uint8[16], scale byte)."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64).reshape(32))
+    data = np.zeros(16, dtype=np.uint8)
+    sc = np.zeros(1, dtype=np.uint8)
+    lib().oracle_mxfp4_encode_block(_ptr(v), _ptr(data), _ptr(sc))
+    return data, int(sc[0])
+
+
+def write_kv_mxfp4(key, value, slot_mapping, key_cache, value_cache, key_scale, value_scale):
+    """MXFP4 cache write: key/value bf16 [N, Hkv, D] (CPU tensors or uint16 arrays),
+    slot_mapping int32 [N], caches uint8 [blocks, Hkv, page, D/2] and scales
+    uint8 [blocks, Hkv, page, D/32]. Returns new (key_cache, value_cache,
+    key_scale, value_scale) numpy arrays; the inputs are not modified."""
+    k, v = _np(key), _np(value)
+    N, H, D = k.shape
+    if v.shape != k.shape:
+        raise ValueError("key and value shapes differ")
+    slots = np.ascontiguousarray(_np(slot_mapping).astype(np.int32).reshape(N))
+    kc, vc, ks, vs = (np.array(_np(a), dtype=np.uint8, copy=True) for a in (key_cache, value_cache, key_scale,
+                                                                               value_scale))
+    nb, hh, pg = kc.shape[0], kc.shape[1], kc.shape[2]
+    if hh != H or kc.shape[3] * 2 != D or vc.shape != kc.shape or ks.shape != (nb, H, pg, D // 32) or \
+            vs.shape != ks.shape:
+        raise ValueError("cache shapes do not match key/value")
+    rc = lib().oracle_write_kv_mxfp4(int(N), int(H), int(D), int(pg), int(nb), _ptr(k.view(np.uint16)),
+                                     _ptr(v.view(np.uint16)), _ptr(slots), _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs))
+    if rc != 0:
+        raise ValueError("oracle rejected the KV-write description (rc=%d)" % rc)
+    return kc, vc, ks, vs
 
 
 def q_row_exponent(amax):

@@ -41,9 +41,14 @@
  *   - a sliding window of W > 0 tokens keeps t >= e_i - W as well, so query
  *     token i attends to [max(0, e_i - W), e_i); an empty range gives o = 0.
  *
+ * The MXFP4 cache write (oracle_write_kv_mxfp4) encodes each 32-element
+ * block with the OCP Microscaling conversion; its readings are stated there.
+ *
  * Parity pins live in the test suite: brute-force dense attention, softmax
  * normalisation, context_len = 1, split/merge invariance, page-permutation
- * invariance and decoder tables checked against library casts.
+ * invariance, decoder tables checked against library casts, and for the
+ * encoder a hand-derived rounding table, exact round trips of representable
+ * blocks and the scale range the conversion guarantees.
  */
 #include <math.h>
 #include <stdint.h>
@@ -184,6 +189,118 @@ int oracle_q_row_exponent(double amax)
     while (amax > ldexp(448.0, e))
         e++;
     return e;
+}
+
+/* Round an fp64 value to OCP MX e2m1, nearest with ties to the even code,
+ * saturating to +-6. Brute force over the 8 non-negative codes; the sign bit is
+ * the sign of x (so small negative values give the code of -0). */
+uint8_t oracle_f64_to_e2m1_rne_sat(double x)
+{
+    uint8_t sign = signbit(x) ? 0x8 : 0;
+    double ax = fabs(x);
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c <= 7; c++) {
+        double d = fabs(oracle_e2m1_to_f64((uint8_t)c) - ax);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            bestd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/*
+ * oracle_mxfp4_encode_block: one 32-element block to MXFP4, following the OCP
+ * Microscaling (MX) v1.0 conversion from scalars to an MX block:
+ *   shared exponent E = floor(log2(max_i |v_i|)) - 2   (2 = largest e2m1 exponent);
+ *   scale byte = E + 127;
+ *   element i = e2m1_rne_sat(v_i / 2^E), packed two per byte, element 2k in
+ *   the low nibble of byte k.
+ * Readings taken where neither the pages nor the format fix the case:
+ *   E is clamped to [-126, 127], not the format's [-127, 127]: the MXFP4
+ *   decode supports scale bytes 1..254 in the rows it reads (ROCm/aiter PR
+ *   #7056, "Summary"), so a finite block never gets byte 0; an all-zero block
+ *   (log2 0 = -inf) gets the bottom of the range, byte 1, and zero elements;
+ *   a block holding NaN or an infinity gets scale byte 0xFF (the e8m0 NaN)
+ *   and zero elements, so every element decodes to NaN.
+ */
+void oracle_mxfp4_encode_block(const double v[32], uint8_t data[16], uint8_t* scale)
+{
+    double amax = 0.0;
+    int finite = 1;
+    for (int i = 0; i < 32; i++) {
+        if (!isfinite(v[i]))
+            finite = 0;
+        else if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    }
+    memset(data, 0, 16);
+    if (!finite) {
+        *scale = 0xFF;
+        return;
+    }
+    int E = -126;
+    if (amax > 0.0) {
+        int e2;
+        frexp(amax, &e2); /* amax = f * 2^e2 with f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+        E = (e2 - 1) - 2;
+        if (E < -126)
+            E = -126;
+        if (E > 127)
+            E = 127;
+    }
+    *scale = (uint8_t)(E + 127);
+    for (int i = 0; i < 32; i++) {
+        uint8_t c = oracle_f64_to_e2m1_rne_sat(ldexp(v[i], -E));
+        data[i / 2] |= (uint8_t)((i & 1) ? (c << 4) : c);
+    }
+}
+
+/*
+ * oracle_write_kv_mxfp4: store new K and V rows into MXFP4 paged caches (the
+ * cache write that produces the pages the MXFP4 decode reads; ROCm/aiter PR
+ * #7056, "Summary": K/V pages of e2m1 data [blocks][Hkv][page][D/2] with e8m0
+ * scales [blocks][Hkv][page][D/32], written by a separate KV-write kernel).
+ *   key, value: bf16 bits [N][Hkv][D];  slots: int32 [N];
+ *   token n with 0 <= slots[n] < num_blocks * page_size goes to page
+ *   slots[n] / page_size, row slots[n] % page_size, for every KV head; other
+ *   slot values (the usual -1 for padding) write nothing.
+ *   Every 32-element block of a row is encoded by oracle_mxfp4_encode_block.
+ * Bytes of rows no token maps to are left as they were. If two tokens map to
+ * one slot the later token wins. Returns 0, or 1 for an invalid description.
+ */
+int oracle_write_kv_mxfp4(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                          int32_t num_blocks, const uint16_t* key, const uint16_t* value, const int32_t* slots,
+                          uint8_t* key_cache, uint8_t* value_cache, uint8_t* key_scale, uint8_t* value_scale)
+{
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 32 || head_dim % 32 != 0 || page_size < 1 ||
+        num_blocks < 1)
+        return OR_EINVAL;
+    const int64_t nslots = (int64_t)num_blocks * page_size;
+    const int nblk = head_dim / 32;
+    for (int64_t n = 0; n < num_tokens; n++) {
+        const int64_t s = slots[n];
+        if (s < 0 || s >= nslots)
+            continue;
+        const int64_t page = s / page_size, row = s % page_size;
+        for (int h = 0; h < num_kv_heads; h++) {
+            const int64_t src = (n * num_kv_heads + h) * (int64_t)head_dim;
+            const int64_t dst_row = (page * num_kv_heads + h) * (int64_t)page_size + row;
+            for (int j = 0; j < nblk; j++) {
+                double v[32];
+                for (int t = 0; t < 2; t++) {
+                    const uint16_t* in = t == 0 ? key : value;
+                    uint8_t* cache = t == 0 ? key_cache : value_cache;
+                    uint8_t* sc = t == 0 ? key_scale : value_scale;
+                    for (int i = 0; i < 32; i++)
+                        v[i] = oracle_bf16_to_f64(in[src + 32 * j + i]);
+                    oracle_mxfp4_encode_block(v, cache + dst_row * (head_dim / 2) + 16 * j, sc + dst_row * nblk + j);
+                }
+            }
+        }
+    }
+    return OR_OK;
 }
 
 /* ------------------------------------------------------------- cache reads */
