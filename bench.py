@@ -25,6 +25,9 @@ protocol: a 1 GiB buffer is read before each call (the last-level cache is
 256 MB; a read leaves clean lines, where a write would leave dirty lines for
 the decode to write back), and the median of the per-call event times is
 reported, for pa_decode with its plan and for the plan-free pa_decode_direct.
+With --all or --kv-write, the MXFP4 KV-cache write (pa_write_kv_mxfp4) is timed
+the same way on its two workloads: the pages of the long MXFP4 decode workload
+written in one call, and the one-token-per-sequence write of a decode step.
 """
 from __future__ import annotations
 
@@ -238,6 +241,57 @@ def time_all(steps, warmup):
     return rows
 
 
+def time_writes(steps, warmup):
+    """Per MXFP4 cache-write workload: cold-cache median and warm mean us per
+    pa_write_kv_mxfp4 call (one kernel on torch's current stream), and the
+    algorithmic GB/s: valid tokens x KV heads x (4 D read + 2 (D/2 + D/32) written)."""
+    import statistics
+
+    import torch
+
+    import paged_attention_decode_token_amd as pa
+    from paged_attention_decode_token_amd import inputs as I
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+    rows = {}
+    for spec in I.WRITE_FULL:
+        case = I.make_write_case(spec, device="cuda")
+        args = (case.key, case.value, case.slot_mapping, case.key_cache, case.value_cache, case.key_scale,
+                case.value_scale)
+
+        def call():
+            pa.pa_write_kv_mxfp4(*args)
+
+        for _ in range(warmup):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            torch.amax(flush, dim=0, out=flush_out)
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+        a, b = ev[0]
+        a.record()
+        for _ in range(steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        us_warm = a.elapsed_time(b) * 1e3 / steps
+        nbytes = case.bytes_moved()
+        gbps = nbytes / (us * 1e-6) / 1e9
+        rows[spec.name] = {"us_per_call": round(us, 2), "warm_us_per_call": round(us_warm, 2),
+                           "tokens": case.num_tokens, "valid_tokens": case.valid_tokens(), "bytes": nbytes,
+                           "GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1)}
+        print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  warm %8.2f us  tokens %d" % (
+            spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, us_warm, case.num_tokens), file=sys.stderr, flush=True)
+        del args, case
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +300,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload (one pa_decode call each) and print a table to stderr")
+    ap.add_argument("--kv-write", action="store_true",
+                    help="also time the MXFP4 cache-write workloads (implied by --all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -356,10 +412,13 @@ def main():
                      "timing": "library HIP events around each tile launch, second pass of the timed steps "
                                "(%.4f ms per step with the events)" % ms_instr},
     }
-    if args.all:
+    if args.all or args.kv_write:
         del variants
         torch.cuda.empty_cache()
+    if args.all:
         res["all_workloads"] = time_all(args.steps, args.warmup)
+    if args.all or args.kv_write:
+        res["kv_write"] = time_writes(args.steps, args.warmup)
     if not args.no_cpu:
         res["cpu_baseline"] = time_cpu_oracle(I.make_case(I.BF16_P64))
     else:

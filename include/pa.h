@@ -205,6 +205,49 @@ pa_status pa_decode_direct(const pa_problem* problem, const void* query, const v
                            const void* value_cache, const void* k_scale, const void* v_scale,
                            const int32_t* block_tables, const int32_t* context_lens, void* out, pa_stream_t stream);
 
+/*
+ * pa_write_kv_mxfp4 -- the MXFP4 KV-cache write: quantize num_tokens new K and V
+ * rows and store them in the paged MXFP4 caches that pa_decode reads (ROCm/aiter
+ * PR #7056, "Summary": the MXFP4 pages come from a separate KV-write kernel, as
+ * e2m1 data with one e8m0 scale per 32 elements along head_dim).
+ *
+ * Each 32-element block of a row is encoded with the OCP Microscaling v1.0
+ * conversion: E = floor(log2 max|v|) - 2 (e2m1's largest exponent is 2), scale
+ * byte E + 127, elements v / 2^E rounded to nearest even in e2m1 and saturated
+ * to +-6; element 2k in the low nibble of byte k. E is clamped to [-126, 127], so
+ * every finite block gets a scale byte in 1..254 (an all-zero block gets 1). A
+ * block holding NaN or an infinity gets scale byte 0xFF (the e8m0 NaN) and zero
+ * data.
+ *
+ *   key, value          bf16 [num_tokens][num_kv_heads][head_dim], contiguous,
+ *                       16-byte aligned, device memory.
+ *   slot_mapping        int32 [num_tokens], device: token n goes to page
+ *                       slot / page_size, row slot % page_size of every KV head.
+ *                       Slots outside [0, num_blocks * page_size) (e.g. -1 for
+ *                       padding) write nothing. A slot may appear at most once
+ *                       per call; with duplicates the row's content is unspecified.
+ *   key_cache, value_cache   uint8 [num_blocks][num_kv_heads][page_size][head_dim / 2]
+ *   key_scale, value_scale   uint8 [num_blocks][num_kv_heads][page_size][head_dim / 32]
+ *                       device memory, caches 16-byte aligned; rows no token maps
+ *                       to are not touched.
+ *
+ * head_dim must be 64, 128 or 256 (pa_decode reads MXFP4 at 128), page_size >= 1,
+ * num_blocks * page_size < 2^31 and num_tokens * num_kv_heads * head_dim < 2^34.
+ * Enqueued on `stream`; nothing is allocated or synchronized. num_tokens == 0 is
+ * a no-op.
+ */
+typedef struct pa_kv_write_problem {
+    int32_t num_tokens;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_blocks;
+} pa_kv_write_problem;
+
+pa_status pa_write_kv_mxfp4(const pa_kv_write_problem* problem, const void* key, const void* value,
+                            const int32_t* slot_mapping, void* key_cache, void* value_cache, void* key_scale,
+                            void* value_scale, pa_stream_t stream);
+
 /* Release a plan and its device workspace (NULL-safe). Synchronizes the device. */
 void pa_plan_destroy(pa_plan_t* plan);
 

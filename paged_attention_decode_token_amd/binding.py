@@ -47,7 +47,11 @@ class pa_plan_info(ctypes.Structure):
         "num_tasks", "max_parts", "total_parts", "tiles_per_task", "merge_needed", "num_cus", "slots")]
 
 
-EXPORTS = ["pa_plan", "pa_decode", "pa_decode_direct", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
+class pa_kv_write_problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("num_tokens", "num_kv_heads", "head_dim", "page_size", "num_blocks")]
+
+
+EXPORTS = ["pa_plan", "pa_decode", "pa_decode_direct", "pa_write_kv_mxfp4", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
            "pa_plan_host", "pa_plan_set_timing", "pa_plan_read_timing", "pa_last_error", "pa_version"]
 
 _lib = None
@@ -69,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.argtypes = [vp] * 10
     L.pa_decode_direct.restype = ctypes.c_int
     L.pa_decode_direct.argtypes = [P(pa_problem)] + [vp] * 9
+    L.pa_write_kv_mxfp4.restype = ctypes.c_int
+    L.pa_write_kv_mxfp4.argtypes = [P(pa_kv_write_problem)] + [vp] * 8
     L.pa_plan_destroy.restype = None
     L.pa_plan_destroy.argtypes = [vp]
     L.pa_plan_workspace_bytes.restype = ctypes.c_size_t
@@ -254,3 +260,36 @@ def decode_case(case, plan=None, out=None, stream=None, **problem_over):
     pa_decode(plan, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"], d["block_tables"],
               d["context_lens"], out, stream)
     return out, plan
+
+
+def pa_write_kv_mxfp4(key, value, slot_mapping, key_cache, value_cache, key_scale, value_scale, stream=None,
+                      problem: Optional[pa_kv_write_problem] = None):
+    """Enqueue the MXFP4 KV-cache write on `stream`.
+
+    key, value: bf16 [num_tokens, Hkv, D]; slot_mapping: int32 [num_tokens];
+    key_cache, value_cache: uint8 [blocks, Hkv, page, D/2]; key_scale,
+    value_scale: uint8 [blocks, Hkv, page, D/32]. The sizes come from the
+    tensors unless `problem` is given (then it is passed through as is)."""
+    if problem is None:
+        if key.dim() != 3 or key_cache.dim() != 4:
+            raise ValueError("key must be [tokens, heads, head_dim] and key_cache [blocks, heads, page, head_dim/2]")
+        if key.dtype != torch.bfloat16 or value.dtype != torch.bfloat16:
+            raise ValueError("key and value must be bfloat16")
+        if slot_mapping.dtype != torch.int32:
+            raise ValueError("slot_mapping must be int32")
+        for t, name in ((key_cache, "key_cache"), (value_cache, "value_cache"), (key_scale, "key_scale"),
+                        (value_scale, "value_scale")):
+            if t.dtype != torch.uint8:
+                raise ValueError("%s must be uint8" % name)
+        N, H, D = key.shape
+        NB, HC, PG, DB = key_cache.shape
+        if (value.shape != key.shape or tuple(slot_mapping.shape) != (N,) or HC != H or DB * 2 != D
+                or value_cache.shape != key_cache.shape or tuple(key_scale.shape) != (NB, H, PG, D // 32)
+                or value_scale.shape != key_scale.shape):
+            raise ValueError("inconsistent shapes for the MXFP4 KV write")
+        problem = pa_kv_write_problem(N, H, D, PG, NB)
+    st = lib().pa_write_kv_mxfp4(ctypes.byref(problem), _dev(key, "key"), _dev(value, "value"),
+                                 _dev(slot_mapping, "slot_mapping"), _dev(key_cache, "key_cache"),
+                                 _dev(value_cache, "value_cache"), _dev(key_scale, "key_scale"),
+                                 _dev(value_scale, "value_scale"), ctypes.c_void_p(_stream_ptr(stream)))
+    _check(st)

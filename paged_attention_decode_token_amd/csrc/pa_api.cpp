@@ -569,6 +569,48 @@ pa_status pa_decode_direct(const pa_problem* problem, const void* query, const v
     return PA_OK;
 }
 
+pa_status pa_write_kv_mxfp4(const pa_kv_write_problem* problem, const void* key, const void* value,
+                            const int32_t* slot_mapping, void* key_cache, void* value_cache, void* key_scale,
+                            void* value_scale, pa_stream_t stream) {
+    if (!problem) return fail(PA_ERR_INVALID_ARG, "problem is NULL");
+    const pa_kv_write_problem& p = *problem;
+    if (p.num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+    if (p.num_kv_heads < 1 || p.page_size < 1 || p.num_blocks < 1)
+        return fail(PA_ERR_INVALID_ARG, "num_kv_heads, page_size and num_blocks must be >= 1");
+    if (p.head_dim != 64 && p.head_dim != 128 && p.head_dim != 256)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128, 256)", p.head_dim);
+    if ((long long)p.num_blocks * p.page_size > 0x7FFFFFFFLL)
+        return fail(PA_ERR_UNSUPPORTED, "num_blocks * page_size exceeds 2^31 - 1 slots");
+    const long long elems = (long long)p.num_tokens * p.num_kv_heads * p.head_dim;
+    if (elems >= (1LL << 34)) return fail(PA_ERR_UNSUPPORTED, "num_tokens * num_kv_heads * head_dim exceeds 2^34");
+    if (p.num_tokens == 0) return PA_OK;
+    if (!key || !value || !slot_mapping || !key_cache || !value_cache || !key_scale || !value_scale)
+        return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (misaligned(key) || misaligned(value) || misaligned(key_cache) || misaligned(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "key, value and the caches must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(slot_mapping) & 3u)
+        return fail(PA_ERR_INVALID_ARG, "slot_mapping must be 4-byte aligned");
+    DeviceInfo dev;
+    pa_status st = probe_device(&dev);
+    if (st != PA_OK) return st;
+    if (!dev.gfx950) return fail(PA_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 only", dev.device, dev.arch.c_str());
+    pa::KvWriteArgs a{};
+    a.key = static_cast<const uint16_t*>(key);
+    a.value = static_cast<const uint16_t*>(value);
+    a.slots = slot_mapping;
+    a.key_cache = static_cast<uint8_t*>(key_cache);
+    a.value_cache = static_cast<uint8_t*>(value_cache);
+    a.key_scale = static_cast<uint8_t*>(key_scale);
+    a.value_scale = static_cast<uint8_t*>(value_scale);
+    a.chunks = (uint32_t)(elems / 8);
+    a.num_kv_heads = p.num_kv_heads;
+    a.page_size = p.page_size;
+    a.num_slots = p.num_blocks * p.page_size;
+    hipError_t e = pa::launch_kv_write_mxfp4(p.head_dim, a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "KV write launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
 pa_status pa_plan_set_timing(pa_plan_t* p, int32_t enable, int32_t max_calls) {
     if (!p) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
     if (enable && max_calls < 1) return fail(PA_ERR_INVALID_ARG, "max_calls must be >= 1");

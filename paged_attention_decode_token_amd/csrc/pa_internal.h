@@ -42,6 +42,22 @@ struct KernelKey {
     int win;  // causal rows (qlen > 1) or a sliding window
 };
 
+// MXFP4 KV-cache write: one 16-byte chunk (8 elements) of K and of V per lane.
+struct KvWriteArgs {
+    const uint16_t* key;    // bf16 [tokens][Hkv][D]
+    const uint16_t* value;
+    const int32_t* slots;   // [tokens]
+    uint8_t* key_cache;     // [blocks][Hkv][page][D/2]
+    uint8_t* value_cache;
+    uint8_t* key_scale;     // [blocks][Hkv][page][D/32]
+    uint8_t* value_scale;
+    uint32_t chunks;        // tokens * Hkv * D / 8
+    int32_t num_kv_heads, page_size, num_slots;
+};
+
+// Launch the KV write for head_dim 64, 128 or 256 (hipErrorInvalidValue otherwise).
+hipError_t launch_kv_write_mxfp4(int head_dim, const KvWriteArgs& args, hipStream_t stream);
+
 // Launch the tile kernel for `key` (returns hipErrorInvalidValue for a key with
 // no compiled instance).
 hipError_t launch_tile(const KernelKey& key, const TileArgs& args, int num_tasks, hipStream_t stream);

@@ -15,6 +15,11 @@ Layouts (the same ones the C ABI documents):
   block_tables   [num_seqs, max_blocks_per_seq] int32
   context_lens   [num_seqs] int32
 
+MXFP4 cache-write inputs (WriteSpec / make_write_case):
+  key, value     [num_tokens, Hkv, D]           bf16 rows to store
+  slot_mapping   [num_tokens] int32             page * page_size + row, -1 for padding
+  caches/scales  as the MXFP4 layouts above, holding random stale bytes
+
 Structure (ROCm/aiter PR #7092, section "Tests"): each sequence's pages are the
 next ceil(L/page) entries of a seeded permutation of pages 1..N, so block 0 is
 never owned; every table row ends with at least 2 padded columns that point to
@@ -303,6 +308,125 @@ def make_case(spec: Spec, fill: Optional[str] = None, seed: Optional[int] = None
                 softmax_scale=0.0, query=query, key_cache=K, value_cache=V, k_scale=k_scale, v_scale=v_scale,
                 block_tables=bt, context_lens=torch.tensor(lens, dtype=torch.int32), causal=spec.causal,
                 window=spec.window)
+
+
+# ---------------------------------------------------------- MXFP4 cache write
+
+@dataclasses.dataclass(frozen=True)
+class WriteSpec:
+    name: str
+    num_seqs: int
+    lens: tuple  # as Spec.lens
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    mode: str  # "fill": positions [0, L) of every sequence (a prefill); "step": position L - 1 only (a decode step)
+    pad_tokens: int = 0  # trailing tokens with slot -1
+    seed: int = 0
+
+    def replace(self, **kw) -> "WriteSpec":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclasses.dataclass
+class WriteCase:
+    spec: WriteSpec
+    num_tokens: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    num_blocks: int
+    key: torch.Tensor
+    value: torch.Tensor
+    slot_mapping: torch.Tensor
+    key_cache: torch.Tensor
+    value_cache: torch.Tensor
+    key_scale: torch.Tensor
+    value_scale: torch.Tensor
+    block_tables: torch.Tensor
+    context_lens: torch.Tensor
+
+    def valid_tokens(self) -> int:
+        s = self.slot_mapping
+        return int(((s >= 0) & (s < self.num_blocks * self.page_size)).sum())
+
+    def bytes_per_token_head(self) -> int:
+        """HBM bytes per (token, KV head): K and V read as bf16, written as MXFP4."""
+        D = self.head_dim
+        return 2 * 2 * D + 2 * (D // 2 + D // 32)
+
+    def bytes_moved(self) -> int:
+        return self.valid_tokens() * self.num_kv_heads * self.bytes_per_token_head()
+
+
+# The pages of the long MXFP4 decode workload (16 sequences x 131072 tokens,
+# 4 KV heads, head_dim 128, page 128), written in one prefill-sized call, and
+# the one-token-per-sequence write of a decode step on the same cache shape.
+MXFP4_WRITE_FILL = WriteSpec("mxfp4_write_fill_b16_l131072", 16, ("const", 131072), 4, 128, 128, "fill", seed=1012)
+MXFP4_WRITE_STEP = WriteSpec("mxfp4_write_step_b16_l131072", 16, ("const", 131072), 4, 128, 128, "step", seed=1013)
+WRITE_FULL = [MXFP4_WRITE_FILL, MXFP4_WRITE_STEP]
+
+
+def small_write(spec: WriteSpec) -> WriteSpec:
+    """The same structure at oracle-friendly sizes (ragged lengths, padding)."""
+    return spec.replace(name=spec.name + "_small", num_seqs=3, num_kv_heads=2, lens=("fixed", (1, 300, 1100)),
+                        pad_tokens=5)
+
+
+def make_write_case(spec: WriteSpec, device="cpu") -> WriteCase:
+    """Seeded cache-write inputs, drawn on `device`. K rows are N(0,1) times a
+    power of two 2^k, k uniform in [-4, 4], per (KV head, channel), so blocks of
+    one row sit at different scales; V rows are N(0,1). The caches hold random
+    stale bytes, which rows no token maps to must keep."""
+    g = torch.Generator(device=device).manual_seed(spec.seed)
+    B, H, D, PG = spec.num_seqs, spec.num_kv_heads, spec.head_dim, spec.page_size
+    gh = torch.Generator().manual_seed(spec.seed)  # host draws: lengths and the page permutation
+    lens = _lens(Spec("w", B, spec.lens, 1, 1, 1, D, PG, "mxfp4"), gh)
+    npages = [(L + PG - 1) // PG for L in lens]
+    NP = sum(npages)
+    num_blocks = NP + 1
+    width = max(npages + [0]) + 2
+    perm = (torch.randperm(NP, generator=gh) + 1).to(torch.int32) if NP > 0 else torch.zeros(0, dtype=torch.int32)
+    bt = torch.zeros(B, width, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :npages[b]] = perm[off:off + npages[b]]
+        off += npages[b]
+    slots = []
+    for b in range(B):
+        pos = torch.arange(lens[b], dtype=torch.int64) if spec.mode == "fill" else \
+            torch.arange(max(lens[b] - 1, 0), lens[b], dtype=torch.int64)
+        slots.append(bt[b].to(torch.int64)[pos // PG] * PG + pos % PG)
+    slots.append(torch.full((spec.pad_tokens,), -1, dtype=torch.int64))
+    slot_mapping = torch.cat(slots).to(torch.int32).to(device)
+    N = int(slot_mapping.numel())
+
+    def draw_bf16(shape, scale=None):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        flat = out.view(-1)
+        n, step = flat.numel(), 1 << 26
+        row = math.prod(shape[1:]) if len(shape) > 1 else 1
+        for s0 in range(0, n, step):
+            e0 = min(n, s0 + step)
+            x = torch.randn(e0 - s0, generator=g, device=device)
+            if scale is not None:  # per (head, channel) factor, repeated along tokens
+                idx = torch.arange(s0, e0, device=device) % row
+                x = x * scale.view(-1)[idx]
+            flat[s0:e0] = x.to(torch.bfloat16)
+        return out
+
+    kscale = torch.exp2(torch.randint(-4, 5, (H, D), generator=g, device=device).to(torch.float32))
+    key = draw_bf16((N, H, D), kscale)
+    value = draw_bf16((N, H, D))
+
+    def stale(shape):
+        return torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+
+    return WriteCase(spec=spec, num_tokens=N, num_kv_heads=H, head_dim=D, page_size=PG, num_blocks=num_blocks,
+                     key=key, value=value, slot_mapping=slot_mapping,
+                     key_cache=stale((num_blocks, H, PG, D // 2)), value_cache=stale((num_blocks, H, PG, D // 2)),
+                     key_scale=stale((num_blocks, H, PG, D // 32)), value_scale=stale((num_blocks, H, PG, D // 32)),
+                     block_tables=bt, context_lens=torch.tensor(lens, dtype=torch.int32))
 
 
 def _unowned_pairs(bt, lens, PG):

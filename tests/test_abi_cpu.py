@@ -78,6 +78,35 @@ def test_plan_free_refusals_come_before_the_device(kw, status):
     assert B.pa_last_error()
 
 
+def _wprob(**kw):
+    base = dict(num_tokens=8, num_kv_heads=4, head_dim=128, page_size=128, num_blocks=10)
+    base.update(kw)
+    return B.pa_kv_write_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), B.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=512), B.PA_ERR_UNSUPPORTED),
+    (dict(num_tokens=-1), B.PA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), B.PA_ERR_INVALID_ARG),
+    (dict(page_size=0), B.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), B.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=2 ** 24, page_size=256), B.PA_ERR_UNSUPPORTED),  # 2^32 slots
+    (dict(num_tokens=2 ** 27, num_kv_heads=2, head_dim=64), B.PA_ERR_UNSUPPORTED),  # 2^34 elements
+    (dict(), B.PA_ERR_INVALID_ARG),  # a valid problem with NULL pointers
+])
+def test_kv_write_refusals_come_before_the_device(kw, status):
+    """pa_write_kv_mxfp4 checks the descriptor and the pointers before it
+    probes the device: every refusal here returns on a host without one."""
+    st = B.lib().pa_write_kv_mxfp4(B.ctypes.byref(_wprob(**kw)), *([None] * 8))
+    assert st == status
+    assert B.pa_last_error()
+
+
+def test_kv_write_of_no_tokens_is_a_no_op():
+    assert B.lib().pa_write_kv_mxfp4(B.ctypes.byref(_wprob(num_tokens=0)), *([None] * 8)) == B.PA_OK
+
+
 def test_host_length_checks():
     with pytest.raises(B.PaError):
         B.pa_plan_host(_prob(), [10, -1, 30, 40])
