@@ -192,14 +192,17 @@ int oracle_q_row_exponent(double amax)
 }
 
 /* Round an fp64 value to OCP MX e2m1, nearest with ties to the even code,
- * saturating to +-6. Brute force over the 8 non-negative codes; the sign bit is
- * the sign of x (so small negative values give the code of -0). */
+ * saturating to +-6: every magnitude at or above 6 gives the largest code.
+ * Below that, brute force over the 8 non-negative codes. The sign bit is the
+ * sign of x (so small negative values give the code of -0). */
 uint8_t oracle_f64_to_e2m1_rne_sat(double x)
 {
     uint8_t sign = signbit(x) ? 0x8 : 0;
     double ax = fabs(x);
     int best = 0;
     double bestd = INFINITY;
+    if (ax >= 6.0)
+        return (uint8_t)(sign | 7);
     for (int c = 0; c <= 7; c++) {
         double d = fabs(oracle_e2m1_to_f64((uint8_t)c) - ax);
         if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {

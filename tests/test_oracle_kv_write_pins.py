@@ -77,6 +77,14 @@ def test_e2m1_scalar_encoder_rounds_ties_to_even():
         assert oracle.f64_to_e2m1(E2M1[c]) == c
 
 
+def test_e2m1_scalar_encoder_saturates_every_large_magnitude():
+    # saturation: anything at or beyond the largest magnitude, 6, takes code 7,
+    # however far beyond (distances to the grid lose precision there)
+    for x in (6.0, 6.5, 7.99, 8.0, 1e6, 2.0 ** 60, 7.26e16, 1e300, float("inf")):
+        assert oracle.f64_to_e2m1(x) == 7
+        assert oracle.f64_to_e2m1(-x) == 15
+
+
 def test_round_trip_of_representable_blocks_is_exact():
     rng = np.random.default_rng(7)
     for _ in range(400):
