@@ -47,7 +47,7 @@ METRIC = "KV-read HBM GB/s and % of peak; µs per pa_decode call per config"
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("pa_kernels.hip", "pa_internal.h"):
+    for f in ("pa_kernels.hip", "pa_kv_write.hip", "pa_internal.h"):
         with open(os.path.join(ROOT, "paged_attention_decode_token_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -99,6 +99,17 @@ def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
                     vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         return vals
 
+    def by_grid(path, counter, key):
+        """{grid size: [values]} of the dispatches of the one kernel matching key."""
+        vals = defaultdict(list)
+        names = set()
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and key in r["Kernel_Name"]:
+                    names.add(r["Kernel_Name"])
+                    vals[int(r["Grid_Size"])].append(float(r["Counter_Value"]))
+        return vals if len(names) == 1 else {}
+
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
 
     def one(vals, key):
@@ -123,6 +134,24 @@ def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
                               "hbm_write_bytes_per_launch": round(wr), "hbm_bytes_per_launch": round(rd + wr),
                               "algorithmic_bytes": alg}
         lines.append("| %s | %s | %d | %.4g | %.4g | %.4g | %.4f |" % (spec.name, tag, len(fv), rd, wr, alg, rd / alg))
+    # the MXFP4 cache write, when the run included it (bench.py --kv-write):
+    # its prefill-sized workload is the launch with the largest grid
+    fg, wg = by_grid(fetch_csv, "FETCH_SIZE", "pa_kv_write_mxfp4_kernel"), by_grid(write_csv, "WRITE_SIZE",
+                                                                                  "pa_kv_write_mxfp4_kernel")
+    if fg and wg:
+        grid = max(fg)
+        fv, wv = fg[grid], wg[grid]
+        rd = sum(fv) / len(fv) * 1024 * f_factor
+        wr = sum(wv) / len(wv) * 1024 * w_factor
+        spec = I.MXFP4_WRITE_FILL
+        alg = I.write_bytes(spec)
+        alg_rd = I.write_bytes(spec, "read")
+        kernels[spec.name] = {"kernel": "pa_kv_write_mxfp4_kernel<%d>" % spec.head_dim, "dispatches": len(fv),
+                              "hbm_read_bytes_per_launch": round(rd), "hbm_write_bytes_per_launch": round(wr),
+                              "hbm_bytes_per_launch": round(rd + wr), "algorithmic_bytes": alg,
+                              "algorithmic_read_bytes": alg_rd}
+        lines.append("| %s | %s | %d | %.4g | %.4g | %.4g | %.4f |" % (
+            spec.name, kernels[spec.name]["kernel"], len(fv), rd, wr, alg, rd / alg_rd))
     doc = {"kernel_source": kernel_source_hash(), "fetch_factor": round(f_factor, 4),
            "write_factor": round(w_factor, 4), "kernels": kernels}
     with open(out_json, "w") as fh:
@@ -284,7 +313,8 @@ def time_writes(steps, warmup):
         gbps = nbytes / (us * 1e-6) / 1e9
         rows[spec.name] = {"us_per_call": round(us, 2), "warm_us_per_call": round(us_warm, 2),
                            "tokens": case.num_tokens, "valid_tokens": case.valid_tokens(), "bytes": nbytes,
-                           "GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1)}
+                           "GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1),
+                           "traffic": load_traffic(spec.name)}
         print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  warm %8.2f us  tokens %d" % (
             spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, us_warm, case.num_tokens), file=sys.stderr, flush=True)
         del args, case

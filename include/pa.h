@@ -228,8 +228,8 @@ pa_status pa_decode_direct(const pa_problem* problem, const void* query, const v
  *                       per call; with duplicates the row's content is unspecified.
  *   key_cache, value_cache   uint8 [num_blocks][num_kv_heads][page_size][head_dim / 2]
  *   key_scale, value_scale   uint8 [num_blocks][num_kv_heads][page_size][head_dim / 32]
- *                       device memory, caches 16-byte aligned; rows no token maps
- *                       to are not touched.
+ *                       device memory, caches and scale tables 16-byte aligned;
+ *                       rows no token maps to are not touched.
  *
  * head_dim must be 64, 128 or 256 (pa_decode reads MXFP4 at 128), page_size >= 1,
  * num_blocks * page_size < 2^31 and num_tokens * num_kv_heads * head_dim < 2^34.

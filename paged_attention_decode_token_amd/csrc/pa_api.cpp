@@ -586,8 +586,9 @@ pa_status pa_write_kv_mxfp4(const pa_kv_write_problem* problem, const void* key,
     if (p.num_tokens == 0) return PA_OK;
     if (!key || !value || !slot_mapping || !key_cache || !value_cache || !key_scale || !value_scale)
         return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
-    if (misaligned(key) || misaligned(value) || misaligned(key_cache) || misaligned(value_cache))
-        return fail(PA_ERR_INVALID_ARG, "key, value and the caches must be 16-byte aligned");
+    if (misaligned(key) || misaligned(value) || misaligned(key_cache) || misaligned(value_cache) ||
+        misaligned(key_scale) || misaligned(value_scale))
+        return fail(PA_ERR_INVALID_ARG, "key, value, the caches and the scale tables must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(slot_mapping) & 3u)
         return fail(PA_ERR_INVALID_ARG, "slot_mapping must be 4-byte aligned");
     DeviceInfo dev;
@@ -602,10 +603,17 @@ pa_status pa_write_kv_mxfp4(const pa_kv_write_problem* problem, const void* key,
     a.value_cache = static_cast<uint8_t*>(value_cache);
     a.key_scale = static_cast<uint8_t*>(key_scale);
     a.value_scale = static_cast<uint8_t*>(value_scale);
-    a.chunks = (uint32_t)(elems / 8);
+    const long long tpw = 64 / (p.head_dim / 8);  // tokens per wave
+    a.wave_tasks = (uint32_t)(((long long)p.num_tokens + tpw - 1) / tpw * p.num_kv_heads);
+    a.num_tokens = p.num_tokens;
     a.num_kv_heads = p.num_kv_heads;
     a.page_size = p.page_size;
     a.num_slots = p.num_blocks * p.page_size;
+    const auto log2_exact = [](int32_t v) {
+        return (v & (v - 1)) == 0 ? __builtin_ctz((unsigned)v) : -1;
+    };
+    a.heads_shift = log2_exact(p.num_kv_heads);
+    a.page_shift = log2_exact(p.page_size);
     hipError_t e = pa::launch_kv_write_mxfp4(p.head_dim, a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "KV write launch failed: %s", hipGetErrorString(e));
     return PA_OK;

@@ -42,7 +42,8 @@ struct KernelKey {
     int win;  // causal rows (qlen > 1) or a sliding window
 };
 
-// MXFP4 KV-cache write: one 16-byte chunk (8 elements) of K and of V per lane.
+// MXFP4 KV-cache write: one 16-byte chunk (8 elements) of K and of V per lane,
+// one wave per (group of 64 / (D / 8) tokens, KV head).
 struct KvWriteArgs {
     const uint16_t* key;    // bf16 [tokens][Hkv][D]
     const uint16_t* value;
@@ -51,8 +52,9 @@ struct KvWriteArgs {
     uint8_t* value_cache;
     uint8_t* key_scale;     // [blocks][Hkv][page][D/32]
     uint8_t* value_scale;
-    uint32_t chunks;        // tokens * Hkv * D / 8
-    int32_t num_kv_heads, page_size, num_slots;
+    uint32_t wave_tasks;    // ceil(tokens / (64 / (D / 8))) * Hkv
+    int32_t num_tokens, num_kv_heads, page_size, num_slots;
+    int32_t heads_shift, page_shift;  // log2 of Hkv / page_size when a power of two, else -1
 };
 
 // Launch the KV write for head_dim 64, 128 or 256 (hipErrorInvalidValue otherwise).

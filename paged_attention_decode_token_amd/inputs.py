@@ -367,6 +367,17 @@ MXFP4_WRITE_STEP = WriteSpec("mxfp4_write_step_b16_l131072", 16, ("const", 13107
 WRITE_FULL = [MXFP4_WRITE_FILL, MXFP4_WRITE_STEP]
 
 
+def write_bytes(spec: WriteSpec, part: str = "all") -> int:
+    """Algorithmic HBM bytes of one write call of `spec` without building it:
+    valid tokens x KV heads x (4 D read; 2 (D/2 + D/32) written)."""
+    gh = torch.Generator().manual_seed(spec.seed)  # the same first draw as make_write_case
+    lens = _lens(Spec("w", spec.num_seqs, spec.lens, 1, 1, 1, spec.head_dim, spec.page_size, "mxfp4"), gh)
+    tokens = sum(lens) if spec.mode == "fill" else sum(1 for L in lens if L > 0)
+    D = spec.head_dim
+    per = {"read": 4 * D, "write": 2 * (D // 2 + D // 32), "all": 4 * D + 2 * (D // 2 + D // 32)}[part]
+    return tokens * spec.num_kv_heads * per
+
+
 def small_write(spec: WriteSpec) -> WriteSpec:
     """The same structure at oracle-friendly sizes (ragged lengths, padding)."""
     return spec.replace(name=spec.name + "_small", num_seqs=3, num_kv_heads=2, lens=("fixed", (1, 300, 1100)),
