@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_mxfp4_encode_block.argtypes = [vp, vp, vp]
         L.oracle_write_kv_mxfp4.restype = ctypes.c_int
         L.oracle_write_kv_mxfp4.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_mqa_logits_mxfp4.restype = ctypes.c_int
+        L.oracle_mqa_logits_mxfp4.argtypes = [i32] * 8 + [vp] * 11
         L.oracle_q_row_exponent.restype = ctypes.c_int
         L.oracle_q_row_exponent.argtypes = [ctypes.c_double]
         L.oracle_num_threads.restype = ctypes.c_int
@@ -221,6 +223,23 @@ def write_kv_mxfp4(key, value, slot_mapping, key_cache, value_cache, key_scale, 
     if rc != 0:
         raise ValueError("oracle rejected the KV-write description (rc=%d)" % rc)
     return kc, vc, ks, vs
+
+
+def mqa_logits_mxfp4(case, fill=float("nan")):
+    """fp64 sparse-indexer scores of an inputs.MqaCase: (out, mag), both
+    [R, out_stride]; positions no window covers keep `fill`."""
+    R, S = case.num_rows, case.out_stride
+    out = np.full((R, S), fill, dtype=np.float64)
+    mag = np.full((R, S), fill, dtype=np.float64)
+    arrs = [_np(case.q), _np(case.q_scale), np.ascontiguousarray(_np(case.weights).astype(np.float32)),
+            _np(case.k_cache), _np(case.k_scale)] + [np.ascontiguousarray(_np(t).astype(np.int32)) for t in (
+                case.block_tables, case.row_to_batch, case.local_starts, case.local_ends)]
+    rc = lib().oracle_mqa_logits_mxfp4(int(R), int(case.num_heads), int(case.head_dim), int(case.page_size),
+                                       int(case.num_blocks), int(case.num_seqs), int(case.max_blocks_per_seq),
+                                       int(S), *[_ptr(a) for a in arrs], _ptr(out), _ptr(mag))
+    if rc != 0:
+        raise ValueError("oracle rejected the MQA-logits description (rc=%d)" % rc)
+    return out, mag
 
 
 def q_row_exponent(amax):

@@ -306,6 +306,94 @@ int oracle_write_kv_mxfp4(int32_t num_tokens, int32_t num_kv_heads, int32_t head
     return OR_OK;
 }
 
+/*
+ * oracle_mqa_logits_mxfp4: the sparse indexer's per-token scores over a paged
+ * MXFP4 index-K cache (ROCm/aiter PR #5761, "Unify gfx950+gfx1250 MXFP4 paged
+ * MQA-logits": per query row, logits over the positions of its own window
+ * [local_start, local_end) of the sequence row_to_batch names, K read through
+ * that sequence's block table; one K head shared by all query heads; q and
+ * per-head weights per row; nothing outside the window is written, and a row
+ * of no live sequence writes nothing).
+ * Reading taken where the pages do not print the formula (the published sparse
+ * indexer score, whose per-head weights only make sense with a nonlinearity):
+ *   out[r][t] = sum_h weights[r][h] * relu( sum_d qhat[r][h][d] * khat[t][d] )
+ * with qhat, khat the MXFP4 values (e2m1 times the e8m0 scale of their 32-element
+ * block) and relu(x) = (x < 0 ? 0 : x), so a NaN score (e.g. from an e8m0 NaN
+ * scale) stays NaN.
+ *   q        u8 [R][H][D/2]   q_scale u8 [R][H][D/32]   weights fp32 [R][H]
+ *   k_cache  u8 [NB][PG][D/2] k_scale u8 [NB][PG][D/32]
+ *   block_tables int32 [B][W]; row_to_batch, local_starts, local_ends int32 [R]
+ *   out, mag fp64 [R][out_stride]: for every row r with 0 <= row_to_batch[r] < B,
+ *   positions t in [max(start, 0), min(end, W * PG, out_stride)) get the score,
+ *   and mag (nullable) gets sum_h |weights[r][h]| * sum_d |qhat * khat|, the
+ *   magnitude the rounding error of a finite-precision sum scales with.
+ *   Everything else is left as the caller filled it.
+ * Returns 0, or 1 for an invalid description or a window position whose block
+ * table entry is outside [0, NB).
+ */
+int oracle_mqa_logits_mxfp4(int32_t num_rows, int32_t num_heads, int32_t head_dim, int32_t page_size,
+                            int32_t num_blocks, int32_t num_seqs, int32_t max_blocks_per_seq, int32_t out_stride,
+                            const uint8_t* q, const uint8_t* q_scale, const float* weights, const uint8_t* k_cache,
+                            const uint8_t* k_scale, const int32_t* block_tables, const int32_t* row_to_batch,
+                            const int32_t* local_starts, const int32_t* local_ends, double* out, double* mag)
+{
+    if (num_rows < 0 || num_heads < 1 || head_dim < 32 || head_dim > 512 || head_dim % 32 != 0 ||
+        page_size < 1 || num_blocks < 1 || num_seqs < 0 || max_blocks_per_seq < 0 || out_stride < 0)
+        return OR_EINVAL;
+    const int D = head_dim, nb = head_dim / 32;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int r = 0; r < num_rows; r++) {
+        const int b = row_to_batch[r];
+        if (b < 0 || b >= num_seqs)
+            continue;
+        int64_t t0 = local_starts[r] < 0 ? 0 : local_starts[r];
+        int64_t t1 = local_ends[r];
+        if (t1 > (int64_t)max_blocks_per_seq * page_size)
+            t1 = (int64_t)max_blocks_per_seq * page_size;
+        if (t1 > out_stride)
+            t1 = out_stride;
+        double* qh = (double*)malloc(sizeof(double) * (size_t)num_heads * D);
+        for (int h = 0; h < num_heads; h++)
+            for (int d = 0; d < D; d++) {
+                const int64_t e = ((int64_t)r * num_heads + h) * D + d;
+                const uint8_t byte = q[e / 2];
+                qh[h * D + d] = oracle_e2m1_to_f64((uint8_t)((d & 1) ? byte >> 4 : byte & 0xF)) *
+                                oracle_e8m0_to_f64(q_scale[((int64_t)r * num_heads + h) * nb + d / 32]);
+            }
+        double kh[512];
+        for (int64_t t = t0; t < t1; t++) {
+            const int32_t page = block_tables[(int64_t)b * max_blocks_per_seq + t / page_size];
+            if (page < 0 || page >= num_blocks) {
+                bad = 1;
+                continue;
+            }
+            const int64_t row = (int64_t)page * page_size + t % page_size;
+            for (int d = 0; d < D; d++) {
+                const uint8_t byte = k_cache[row * (D / 2) + d / 2];
+                kh[d] = oracle_e2m1_to_f64((uint8_t)((d & 1) ? byte >> 4 : byte & 0xF)) *
+                        oracle_e8m0_to_f64(k_scale[row * nb + d / 32]);
+            }
+            double acc = 0.0, m = 0.0;
+            for (int h = 0; h < num_heads; h++) {
+                double s = 0.0, sa = 0.0;
+                for (int d = 0; d < D; d++) {
+                    s += qh[h * D + d] * kh[d];
+                    sa += fabs(qh[h * D + d] * kh[d]);
+                }
+                const double w = weights[(int64_t)r * num_heads + h];
+                acc += w * (s < 0.0 ? 0.0 : s);
+                m += fabs(w) * sa;
+            }
+            out[(int64_t)r * out_stride + t] = acc;
+            if (mag)
+                mag[(int64_t)r * out_stride + t] = m;
+        }
+        free(qh);
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
 /* ------------------------------------------------------------- cache reads */
 
 static double kv_elem(const oracle_problem* p, const void* cache, const void* scale_mx, int64_t page, int kvh,

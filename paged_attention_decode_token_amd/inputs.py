@@ -440,6 +440,135 @@ def make_write_case(spec: WriteSpec, device="cpu") -> WriteCase:
                      block_tables=bt, context_lens=torch.tensor(lens, dtype=torch.int32))
 
 
+# ------------------------------------------------- MXFP4 paged MQA logits
+
+@dataclasses.dataclass(frozen=True)
+class MqaSpec:
+    name: str
+    num_seqs: int
+    lens: tuple  # as Spec.lens
+    rows_per_seq: int  # query rows per sequence (1: decode; >1: causal multi-token rows)
+    num_heads: int
+    head_dim: int
+    page_size: int
+    pad_rows: int = 0  # trailing rows of no sequence (row_to_batch -1, empty window)
+    fill: str = "nan"  # bytes of K rows no window covers: "nan" (0xFF data and scale) or "random"
+    seed: int = 0
+
+    def replace(self, **kw) -> "MqaSpec":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclasses.dataclass
+class MqaCase:
+    spec: MqaSpec
+    num_rows: int
+    num_heads: int
+    head_dim: int
+    page_size: int
+    num_blocks: int
+    num_seqs: int
+    max_blocks_per_seq: int
+    out_stride: int
+    q: torch.Tensor            # u8 [R, H, D/2]
+    q_scale: torch.Tensor      # u8 [R, H, D/32]
+    weights: torch.Tensor      # fp32 [R, H]
+    k_cache: torch.Tensor      # u8 [NB, PG, D/2]
+    k_scale: torch.Tensor      # u8 [NB, PG, D/32]
+    block_tables: torch.Tensor  # int32 [B, W]
+    row_to_batch: torch.Tensor  # int32 [R]
+    local_starts: torch.Tensor  # int32 [R]
+    local_ends: torch.Tensor    # int32 [R]
+    context_lens: torch.Tensor  # int32 [B]
+
+    def window_tokens(self) -> int:
+        live = self.row_to_batch >= 0
+        return int((self.local_ends - self.local_starts).clamp(min=0)[live].sum())
+
+    def bytes_per_row_token(self) -> int:
+        """HBM bytes per (row, window position): one K row (data + scales) read, one fp32 score written."""
+        D = self.head_dim
+        return D // 2 + D // 32 + 4
+
+    def bytes_moved(self) -> int:
+        return self.window_tokens() * self.bytes_per_row_token()
+
+
+# The long MXFP4 decode shape as an indexer: 16 sequences of 131072 tokens,
+# one query row each, 64 index heads of 128 (a 4 KB MXFP4 query row), an index
+# cache with 64-token pages; and two causal rows per sequence (a multi-token
+# step) over 32768 tokens.
+MQA_DECODE_LONG = MqaSpec("mqa_mxfp4_h64_p64_b16_l131072", 16, ("const", 131072), 1, 64, 128, 64, seed=1014)
+MQA_MTP2 = MqaSpec("mqa_mxfp4_h64_p64_b16_l32768_rows2", 16, ("const", 32768), 2, 64, 128, 64, pad_rows=3,
+                   seed=1015)
+MQA_FULL = [MQA_DECODE_LONG, MQA_MTP2]
+
+
+def small_mqa(spec: MqaSpec) -> MqaSpec:
+    """Oracle-friendly sizes with ragged lengths, short windows and pad rows."""
+    return spec.replace(name=spec.name + "_small", num_seqs=4, lens=("fixed", (1, 77, 300, 1030)), pad_rows=2)
+
+
+def make_mqa_case(spec: MqaSpec, device="cpu") -> MqaCase:
+    """Seeded MQA-logits inputs. Row i of a sequence of length L with n rows
+    has the causal window [0, L - n + i + 1); pad rows have row_to_batch -1 and
+    an empty window. q and K data bytes are uniform (all 16 e2m1 codes per
+    nibble), q scales uniform in [120, 134], K scales in [118, 136], weights
+    N(0, 1) / 8. K rows that no window covers hold the fill."""
+    g = torch.Generator().manual_seed(spec.seed)
+    B, H, D, PG, n = spec.num_seqs, spec.num_heads, spec.head_dim, spec.page_size, spec.rows_per_seq
+    lens = _lens(Spec("m", B, spec.lens, 1, 1, 1, D, PG, "mxfp4"), g)
+    npages = [(L + PG - 1) // PG for L in lens]
+    NP = sum(npages)
+    num_blocks = NP + 1
+    W = max(npages + [0]) + 2
+    perm = (torch.randperm(NP, generator=g) + 1).to(torch.int32) if NP > 0 else torch.zeros(0, dtype=torch.int32)
+    bt = torch.zeros(B, W, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :npages[b]] = perm[off:off + npages[b]]
+        off += npages[b]
+    rtb, starts, ends = [], [], []
+    for b in range(B):
+        for i in range(n):
+            rtb.append(b)
+            starts.append(0)
+            ends.append(max(lens[b] - n + i + 1, 0))
+    for _ in range(spec.pad_rows):
+        rtb.append(-1)
+        starts.append(0)
+        ends.append(0)
+    R = len(rtb)
+    out_stride = max([e for e in ends] + [0])
+    out_stride = (out_stride + 15) // 16 * 16 + 16
+    gd = torch.Generator(device=device).manual_seed(spec.seed + 7)
+
+    def u8(shape, lo, hi):
+        return torch.randint(lo, hi, shape, generator=gd, device=device, dtype=torch.int32).to(torch.uint8)
+
+    q = u8((R, H, D // 2), 0, 256)
+    q_scale = u8((R, H, D // 32), 120, 135)
+    weights = torch.randn((R, H), generator=gd, device=device) / 8
+    k_cache = u8((num_blocks, PG, D // 2), 0, 256)
+    k_scale = u8((num_blocks, PG, D // 32), 118, 137)
+    if spec.fill == "nan":
+        # every K row outside the sequences' owned tokens: block 0 and last-page tails
+        k_cache[0] = 0xFF
+        k_scale[0] = 0xFF
+        for b in range(B):
+            if lens[b] % PG:
+                last = int(bt[b, npages[b] - 1])
+                k_cache[last, lens[b] % PG:] = 0xFF
+                k_scale[last, lens[b] % PG:] = 0xFF
+    return MqaCase(spec=spec, num_rows=R, num_heads=H, head_dim=D, page_size=PG, num_blocks=num_blocks, num_seqs=B,
+                   max_blocks_per_seq=W, out_stride=out_stride, q=q, q_scale=q_scale, weights=weights,
+                   k_cache=k_cache, k_scale=k_scale, block_tables=bt.to(device),
+                   row_to_batch=torch.tensor(rtb, dtype=torch.int32).to(device),
+                   local_starts=torch.tensor(starts, dtype=torch.int32).to(device),
+                   local_ends=torch.tensor(ends, dtype=torch.int32).to(device),
+                   context_lens=torch.tensor(lens, dtype=torch.int32))
+
+
 def _unowned_pairs(bt, lens, PG):
     """(pages, slots) of every row no sequence owns: all of block 0, then the
     tail of each sequence's last page."""
