@@ -28,6 +28,8 @@ reported, for pa_decode with its plan and for the plan-free pa_decode_direct.
 With --all or --kv-write, the MXFP4 KV-cache write (pa_write_kv_mxfp4) is timed
 the same way on its two workloads: the pages of the long MXFP4 decode workload
 written in one call, and the one-token-per-sequence write of a decode step.
+With --all or --mqa, the MXFP4 paged MQA logits (pa_mqa_logits_mxfp4) is timed
+the same way on its decode and two-row workloads.
 """
 from __future__ import annotations
 
@@ -322,6 +324,54 @@ def time_writes(steps, warmup):
     return rows
 
 
+def time_mqa(steps, warmup):
+    """Per MXFP4 MQA-logits workload: cold-cache median us per pa_mqa_logits_mxfp4
+    call and the algorithmic GB/s: window positions x (one K row of 68 bytes
+    read + one fp32 score written)."""
+    import statistics
+
+    import torch
+
+    import paged_attention_decode_token_amd as pa
+    from paged_attention_decode_token_amd import inputs as I
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+    rows = {}
+    for spec in I.MQA_FULL:
+        case = I.make_mqa_case(spec, device="cuda")
+        out = torch.full((case.num_rows, case.out_stride), float("-inf"), dtype=torch.float32, device="cuda")
+        prob = pa.mqa_problem_of(case)
+        args = (prob, case.q, case.q_scale, case.weights, case.k_cache, case.k_scale, case.block_tables,
+                case.row_to_batch, case.local_starts, case.local_ends, out)
+
+        def call():
+            pa.pa_mqa_logits_mxfp4(*args)
+
+        for _ in range(warmup):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            torch.amax(flush, dim=0, out=flush_out)
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+        nbytes = case.bytes_moved()
+        gbps = nbytes / (us * 1e-6) / 1e9
+        rows[spec.name] = {"us_per_call": round(us, 2), "rows": case.num_rows, "positions": case.window_tokens(),
+                           "bytes": nbytes, "GBps": round(gbps, 1),
+                           "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1),
+                           "tflops": round(case.window_tokens() * case.num_heads * case.head_dim * 2 / (us * 1e-6)
+                                           / 1e12, 1)}
+        print("%-40s %9.2f us  %7.1f GB/s  %5.1f%%  positions %d" % (
+            spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, case.window_tokens()), file=sys.stderr, flush=True)
+        del args, case, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +382,8 @@ def main():
                     help="also time every workload (one pa_decode call each) and print a table to stderr")
     ap.add_argument("--kv-write", action="store_true",
                     help="also time the MXFP4 cache-write workloads (implied by --all)")
+    ap.add_argument("--mqa", action="store_true",
+                    help="also time the MXFP4 paged MQA-logits workloads (implied by --all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -442,13 +494,15 @@ def main():
                      "timing": "library HIP events around each tile launch, second pass of the timed steps "
                                "(%.4f ms per step with the events)" % ms_instr},
     }
-    if args.all or args.kv_write:
+    if args.all or args.kv_write or args.mqa:
         del variants
         torch.cuda.empty_cache()
     if args.all:
         res["all_workloads"] = time_all(args.steps, args.warmup)
     if args.all or args.kv_write:
         res["kv_write"] = time_writes(args.steps, args.warmup)
+    if args.all or args.mqa:
+        res["mqa_logits"] = time_mqa(args.steps, args.warmup)
     if not args.no_cpu:
         res["cpu_baseline"] = time_cpu_oracle(I.make_case(I.BF16_P64))
     else:

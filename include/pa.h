@@ -248,6 +248,54 @@ pa_status pa_write_kv_mxfp4(const pa_kv_write_problem* problem, const void* key,
                             const int32_t* slot_mapping, void* key_cache, void* value_cache, void* key_scale,
                             void* value_scale, pa_stream_t stream);
 
+/*
+ * pa_mqa_logits_mxfp4 -- the sparse indexer's scores over a paged MXFP4 index-K
+ * cache (ROCm/aiter PR #5761, "Unify gfx950+gfx1250 MXFP4 paged MQA-logits":
+ * per query row, scores over the positions of its own window of the sequence
+ * row_to_batch names, one K head shared by all query heads, K read through that
+ * sequence's block table, nothing written outside the window):
+ *
+ *   out[r * out_stride + t] = sum_h weights[r][h] * relu(qhat[r][h] . khat_b(t))
+ *   for t in [max(local_starts[r], 0), min(local_ends[r], W * page_size, out_stride))
+ *
+ * with b = row_to_batch[r], khat_b(t) the K row at page block_tables[b][t / page_size],
+ * slot t % page_size, qhat and khat MXFP4 values (e2m1 times the e8m0 scale of
+ * their 32-element block), and relu(x) = (x < 0 ? 0 : x), which keeps a NaN. The
+ * pages give the op's inputs and contract but not the formula; this is the
+ * published sparse-indexer score. Rows with b outside [0, num_seqs), and empty
+ * windows, write nothing; every other position of out keeps its content.
+ *
+ *   q             uint8 [num_rows][num_heads][head_dim / 2]  e2m1, element 2i low nibble
+ *   q_scale       uint8 [num_rows][num_heads][head_dim / 32] e8m0
+ *   weights       fp32  [num_rows][num_heads]
+ *   k_cache       uint8 [num_blocks][page_size][head_dim / 2]
+ *   k_scale       uint8 [num_blocks][page_size][head_dim / 32]
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq] (W)
+ *   row_to_batch, local_starts, local_ends   int32 [num_rows]
+ *   out           fp32  [num_rows][out_stride]
+ * All device memory; q, weights and k_cache 16-byte aligned, the rest 4-byte.
+ * head_dim must be 128, num_heads 16, 32, 64 or 128, page_size a multiple of 16.
+ * Block-table entries are clamped into [0, num_blocks), so a bad table cannot
+ * fault. The result is fp32; each score is a sum of num_heads weighted products,
+ * rounded in fp32. Enqueued on `stream`; nothing is allocated or synchronized.
+ */
+typedef struct pa_mqa_problem {
+    int32_t num_rows;
+    int32_t num_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_blocks;
+    int32_t num_seqs;
+    int32_t max_blocks_per_seq;
+    int32_t out_stride;
+} pa_mqa_problem;
+
+pa_status pa_mqa_logits_mxfp4(const pa_mqa_problem* problem, const void* q, const void* q_scale,
+                              const float* weights, const void* k_cache, const void* k_scale,
+                              const int32_t* block_tables, const int32_t* row_to_batch,
+                              const int32_t* local_starts, const int32_t* local_ends, float* out,
+                              pa_stream_t stream);
+
 /* Release a plan and its device workspace (NULL-safe). Synchronizes the device. */
 void pa_plan_destroy(pa_plan_t* plan);
 

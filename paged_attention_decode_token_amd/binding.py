@@ -51,7 +51,12 @@ class pa_kv_write_problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("num_tokens", "num_kv_heads", "head_dim", "page_size", "num_blocks")]
 
 
-EXPORTS = ["pa_plan", "pa_decode", "pa_decode_direct", "pa_write_kv_mxfp4", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
+class pa_mqa_problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("num_rows", "num_heads", "head_dim", "page_size", "num_blocks",
+                                              "num_seqs", "max_blocks_per_seq", "out_stride")]
+
+
+EXPORTS = ["pa_plan", "pa_decode", "pa_decode_direct", "pa_write_kv_mxfp4", "pa_mqa_logits_mxfp4", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
            "pa_plan_host", "pa_plan_set_timing", "pa_plan_read_timing", "pa_last_error", "pa_version"]
 
 _lib = None
@@ -75,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_direct.argtypes = [P(pa_problem)] + [vp] * 9
     L.pa_write_kv_mxfp4.restype = ctypes.c_int
     L.pa_write_kv_mxfp4.argtypes = [P(pa_kv_write_problem)] + [vp] * 8
+    L.pa_mqa_logits_mxfp4.restype = ctypes.c_int
+    L.pa_mqa_logits_mxfp4.argtypes = [P(pa_mqa_problem)] + [vp] * 11
     L.pa_plan_destroy.restype = None
     L.pa_plan_destroy.argtypes = [vp]
     L.pa_plan_workspace_bytes.restype = ctypes.c_size_t
@@ -293,3 +300,28 @@ def pa_write_kv_mxfp4(key, value, slot_mapping, key_cache, value_cache, key_scal
                                  _dev(value_cache, "value_cache"), _dev(key_scale, "key_scale"),
                                  _dev(value_scale, "value_scale"), ctypes.c_void_p(_stream_ptr(stream)))
     _check(st)
+
+
+def mqa_problem_of(case) -> pa_mqa_problem:
+    """pa_mqa_problem of a paged_attention_decode_token_amd.inputs.MqaCase."""
+    return pa_mqa_problem(case.num_rows, case.num_heads, case.head_dim, case.page_size, case.num_blocks,
+                          case.num_seqs, case.max_blocks_per_seq, case.out_stride)
+
+
+def pa_mqa_logits_mxfp4(problem: pa_mqa_problem, q, q_scale, weights, k_cache, k_scale, block_tables, row_to_batch,
+                        local_starts, local_ends, out, stream=None):
+    """Enqueue the MXFP4 paged MQA logits on `stream`; writes only window positions of `out`."""
+    for t, name, dt in ((q, "q", torch.uint8), (q_scale, "q_scale", torch.uint8), (weights, "weights", torch.float32),
+                        (k_cache, "k_cache", torch.uint8), (k_scale, "k_scale", torch.uint8),
+                        (block_tables, "block_tables", torch.int32), (row_to_batch, "row_to_batch", torch.int32),
+                        (local_starts, "local_starts", torch.int32), (local_ends, "local_ends", torch.int32),
+                        (out, "out", torch.float32)):
+        if t.dtype != dt:
+            raise ValueError("%s must be %s" % (name, dt))
+    st = lib().pa_mqa_logits_mxfp4(ctypes.byref(problem), _dev(q, "q"), _dev(q_scale, "q_scale"),
+                                   _dev(weights, "weights"), _dev(k_cache, "k_cache"), _dev(k_scale, "k_scale"),
+                                   _dev(block_tables, "block_tables"), _dev(row_to_batch, "row_to_batch"),
+                                   _dev(local_starts, "local_starts"), _dev(local_ends, "local_ends"),
+                                   _dev(out, "out"), ctypes.c_void_p(_stream_ptr(stream)))
+    _check(st)
+    return out

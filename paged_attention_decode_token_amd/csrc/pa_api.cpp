@@ -619,6 +619,69 @@ pa_status pa_write_kv_mxfp4(const pa_kv_write_problem* problem, const void* key,
     return PA_OK;
 }
 
+pa_status pa_mqa_logits_mxfp4(const pa_mqa_problem* problem, const void* q, const void* q_scale,
+                              const float* weights, const void* k_cache, const void* k_scale,
+                              const int32_t* block_tables, const int32_t* row_to_batch,
+                              const int32_t* local_starts, const int32_t* local_ends, float* out,
+                              pa_stream_t stream) {
+    if (!problem) return fail(PA_ERR_INVALID_ARG, "problem is NULL");
+    const pa_mqa_problem& p = *problem;
+    if (p.num_rows < 0 || p.num_seqs < 0 || p.out_stride < 0)
+        return fail(PA_ERR_INVALID_ARG, "num_rows, num_seqs and out_stride must be >= 0");
+    if (p.num_blocks < 1 || p.max_blocks_per_seq < 1 || p.page_size < 1)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks, max_blocks_per_seq and page_size must be >= 1");
+    if (p.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 128)", p.head_dim);
+    if (p.num_heads != 16 && p.num_heads != 32 && p.num_heads != 64 && p.num_heads != 128)
+        return fail(PA_ERR_UNSUPPORTED, "num_heads %d (supported: 16, 32, 64, 128)", p.num_heads);
+    if (p.page_size % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", p.page_size);
+    const long long reach = (long long)p.max_blocks_per_seq * p.page_size;
+    if (reach > 0x7FFFFFFFLL - 512 || (long long)p.num_blocks * p.page_size > 0x7FFFFFFFLL ||
+        p.out_stride > 0x7FFFFFFF - 512)
+        return fail(PA_ERR_UNSUPPORTED, "a table, pool or output row beyond 2^31 positions");
+    const long long max_pos = std::min(reach, (long long)p.out_stride);
+    const long long chunks = (max_pos + 255) / 256;
+    if ((long long)p.num_rows * chunks >= (1LL << 31))
+        return fail(PA_ERR_UNSUPPORTED, "num_rows * ceil(positions / 256) exceeds 2^31");
+    if (p.num_rows == 0 || max_pos == 0) return PA_OK;
+    if (!q || !q_scale || !weights || !k_cache || !k_scale || !block_tables || !row_to_batch || !local_starts ||
+        !local_ends || !out)
+        return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (misaligned(q) || misaligned(weights) || misaligned(k_cache))
+        return fail(PA_ERR_INVALID_ARG, "q, weights and k_cache must be 16-byte aligned");
+    const uintptr_t ors = reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+                          reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(row_to_batch) |
+                          reinterpret_cast<uintptr_t>(local_starts) | reinterpret_cast<uintptr_t>(local_ends) |
+                          reinterpret_cast<uintptr_t>(out);
+    if (ors & 3u) return fail(PA_ERR_INVALID_ARG, "scale tables, index arrays and out must be 4-byte aligned");
+    DeviceInfo dev;
+    pa_status st = probe_device(&dev);
+    if (st != PA_OK) return st;
+    if (!dev.gfx950) return fail(PA_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 only", dev.device, dev.arch.c_str());
+    pa::MqaArgs a{};
+    a.q = static_cast<const uint8_t*>(q);
+    a.q_scale = static_cast<const uint8_t*>(q_scale);
+    a.weights = weights;
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.k_scale = static_cast<const uint8_t*>(k_scale);
+    a.block_tables = block_tables;
+    a.row_to_batch = row_to_batch;
+    a.local_starts = local_starts;
+    a.local_ends = local_ends;
+    a.out = out;
+    a.items = (uint32_t)((long long)p.num_rows * chunks);
+    a.num_rows = p.num_rows;
+    a.page_size = p.page_size;
+    a.page_shift = (p.page_size & (p.page_size - 1)) == 0 ? __builtin_ctz((unsigned)p.page_size) : -1;
+    a.num_blocks = p.num_blocks;
+    a.num_seqs = p.num_seqs;
+    a.max_blocks_per_seq = p.max_blocks_per_seq;
+    a.out_stride = p.out_stride;
+    a.max_pos = (int32_t)max_pos;
+    hipError_t e = pa::launch_mqa_logits_mxfp4(p.num_heads, a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "MQA-logits launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
 pa_status pa_plan_set_timing(pa_plan_t* p, int32_t enable, int32_t max_calls) {
     if (!p) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
     if (enable && max_calls < 1) return fail(PA_ERR_INVALID_ARG, "max_calls must be >= 1");

@@ -60,6 +60,27 @@ struct KvWriteArgs {
 // Launch the KV write for head_dim 64, 128 or 256 (hipErrorInvalidValue otherwise).
 hipError_t launch_kv_write_mxfp4(int head_dim, const KvWriteArgs& args, hipStream_t stream);
 
+// MXFP4 paged MQA logits (head_dim 128): one workgroup per (256-position
+// chunk, row) work item.
+struct MqaArgs {
+    const uint8_t* q;        // [rows][H][64]
+    const uint8_t* q_scale;  // [rows][H][4]
+    const float* weights;    // [rows][H]
+    const uint8_t* k_cache;  // [blocks][page][64]
+    const uint8_t* k_scale;  // [blocks][page][4]
+    const int32_t* block_tables;
+    const int32_t* row_to_batch;
+    const int32_t* local_starts;
+    const int32_t* local_ends;
+    float* out;              // [rows][out_stride]
+    uint32_t items;          // rows * chunks
+    int32_t num_rows, page_size, page_shift, num_blocks, num_seqs, max_blocks_per_seq, out_stride;
+    int32_t max_pos;         // min(max_blocks_per_seq * page_size, out_stride)
+};
+
+// Launch the MQA-logits kernel for 16, 32, 64 or 128 heads (hipErrorInvalidValue otherwise).
+hipError_t launch_mqa_logits_mxfp4(int num_heads, const MqaArgs& args, hipStream_t stream);
+
 // Launch the tile kernel for `key` (returns hipErrorInvalidValue for a key with
 // no compiled instance).
 hipError_t launch_tile(const KernelKey& key, const TileArgs& args, int num_tasks, hipStream_t stream);

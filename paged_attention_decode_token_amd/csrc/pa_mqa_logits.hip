@@ -1,0 +1,141 @@
+// MXFP4 paged MQA logits for gfx950: the sparse indexer's per-token scores
+// (ROCm/aiter PR #5761, "Unify gfx950+gfx1250 MXFP4 paged MQA-logits": per
+// query row, scores over the positions of its window [local_start, local_end)
+// of the sequence row_to_batch names, one K head shared by every query head,
+// K read through the block table; nothing outside the window is written).
+//
+//   out[r][t] = sum_h w[r][h] * relu(qhat[r][h] . khat[t]),  relu(x) = x < 0 ? 0 : x
+//
+// with q and K in MXFP4 (e2m1, one e8m0 scale per 32 elements), head_dim 128.
+// relu keeps a NaN, so a NaN scale reaches the positions that read it.
+//
+// Work: a workgroup takes 256 positions of one row; each wave 64 of them as
+// four 16-token tiles. Per tile and group of 16 heads, one
+// v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 on both sides gives
+// S[head][token]: A = the row's q (16 heads, loaded once per wave), B = the
+// tile's 16 K rows. Lane layouts, measured on gfx950: A lane (m, g) nibble i
+// is k = 32g + i of row m, B lane (n, g) nibble i is k = 32g + i of column n
+// (element 2i in the low nibble), and each lane's scale byte applies to its own
+// 32 elements; C lane (n, g) holds rows 4g .. 4g + 3 of column n. A lane then
+// weights and sums its four heads of every group, two lane swaps add the four
+// lane groups, and lanes 0..15 store the tile's 16 scores.
+//
+// HBM-bound: per (row, position) one K row (64 data + 4 scale bytes) is read
+// and one fp32 score written; the row's q, scales and weights (4.4 KB at 64
+// heads) are read once per workgroup and stay in L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef int mq_i32x8 __attribute__((ext_vector_type(8)));
+typedef float mq_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mq_u32x4 __attribute__((ext_vector_type(4)));
+
+#define MQ_DEV __device__ __forceinline__
+
+constexpr int kMqChunk = 256;   // positions per workgroup
+constexpr uint32_t kMqXcds = 8;  // accelerator complex dies of an MI355X
+
+MQ_DEV uint32_t mq_div(uint32_t x, int32_t d, int32_t shift) {
+    return shift >= 0 ? x >> shift : x / (uint32_t)d;
+}
+
+// HT groups of 16 heads; head_dim 128 (one MFMA per group and tile).
+template <int HT>
+__global__ __launch_bounds__(256) void pa_mqa_logits_mxfp4_kernel(const MqaArgs a) {
+    // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
+    // contiguous range of (chunk, row) work items, rows fastest, so the rows
+    // that share a chunk's K rows meet in one L2. The grid is a multiple of 8.
+    const uint32_t per_xcd = gridDim.x / kMqXcds;
+    const uint32_t item = (blockIdx.x % kMqXcds) * per_xcd + blockIdx.x / kMqXcds;
+    if (item >= a.items) return;
+    const int r = (int)(item % (uint32_t)a.num_rows);
+    const int chunk = (int)(item / (uint32_t)a.num_rows);
+    const int b = a.row_to_batch[r];
+    if (b < 0 || b >= a.num_seqs) return;
+    const int t0 = max(a.local_starts[r], 0);
+    const int t1 = min(a.local_ends[r], a.max_pos);
+    const int c0 = chunk * kMqChunk;
+    if (c0 >= t1 || c0 + kMqChunk <= t0) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int n = lane & 15, g = lane >> 4;
+    const int H = HT * 16;
+
+    // this wave's four tiles: page ids, then K rows and scale bytes
+    const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+    mq_u32x4 kd[4];
+    uint32_t ks[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // positions past the window (up to 255 beyond it) are computed and not
+        // stored: their table column and page id are clamped into range
+        const uint32_t t = (uint32_t)(c0 + 64 * wave + 16 * j + n);
+        const uint32_t colt = mq_div(t, a.page_size, a.page_shift);
+        const uint32_t slot = t - colt * (uint32_t)a.page_size;
+        const uint32_t col = min(colt, (uint32_t)(a.max_blocks_per_seq - 1));
+        const int page = min(max(bt[col], 0), a.num_blocks - 1);
+        const size_t krow = (size_t)page * a.page_size + slot;
+        kd[j] = *reinterpret_cast<const mq_u32x4*>(a.k_cache + krow * 64 + 16 * g);
+        ks[j] = a.k_scale[krow * 4 + g];
+    }
+    // the row's q fragments (head 16i + n, block g) and the weights of the
+    // heads this lane's accumulator rows hold (16i + 4g + 0..3)
+    mq_u32x4 qd[HT];
+    uint32_t qs[HT];
+    mq_f32x4 w[HT];
+#pragma unroll
+    for (int i = 0; i < HT; ++i) {
+        const size_t qrow = (size_t)r * H + 16 * i + n;
+        qd[i] = *reinterpret_cast<const mq_u32x4*>(a.q + qrow * 64 + 16 * g);
+        qs[i] = a.q_scale[qrow * 4 + g];
+        w[i] = *reinterpret_cast<const mq_f32x4*>(a.weights + (size_t)r * H + 16 * i + 4 * g);
+    }
+
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const mq_i32x8 kb = {(int)kd[j].x, (int)kd[j].y, (int)kd[j].z, (int)kd[j].w, 0, 0, 0, 0};
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < HT; ++i) {
+            const mq_i32x8 qa = {(int)qd[i].x, (int)qd[i].y, (int)qd[i].z, (int)qd[i].w, 0, 0, 0, 0};
+            mq_f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, kb, s, 4, 4, 0, (int)qs[i], 0, (int)ks[j]);
+            acc += w[i].x * (s.x < 0.f ? 0.f : s.x);
+            acc += w[i].y * (s.y < 0.f ? 0.f : s.y);
+            acc += w[i].z * (s.z < 0.f ? 0.f : s.z);
+            acc += w[i].w * (s.w < 0.f ? 0.f : s.w);
+        }
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        const int t = c0 + 64 * wave + 16 * j + n;
+        if (g == 0 && t >= t0 && t < t1) a.out[(size_t)r * a.out_stride + t] = acc;
+    }
+}
+
+template <int HT>
+hipError_t launch_h(const MqaArgs& a, hipStream_t stream) {
+    const uint32_t grid = (a.items + kMqXcds - 1) / kMqXcds * kMqXcds;
+    hipLaunchKernelGGL((pa_mqa_logits_mxfp4_kernel<HT>), dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mqa_logits_mxfp4(int num_heads, const MqaArgs& a, hipStream_t stream) {
+    if (a.items == 0) return hipSuccess;
+    switch (num_heads) {
+        case 16: return launch_h<1>(a, stream);
+        case 32: return launch_h<2>(a, stream);
+        case 64: return launch_h<4>(a, stream);
+        case 128: return launch_h<8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pa

@@ -107,6 +107,33 @@ def test_kv_write_of_no_tokens_is_a_no_op():
     assert B.lib().pa_write_kv_mxfp4(B.ctypes.byref(_wprob(num_tokens=0)), *([None] * 8)) == B.PA_OK
 
 
+def _mprob(**kw):
+    base = dict(num_rows=4, num_heads=64, head_dim=128, page_size=64, num_blocks=10, num_seqs=2,
+                max_blocks_per_seq=5, out_stride=400)
+    base.update(kw)
+    return B.pa_mqa_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), B.PA_ERR_UNSUPPORTED),
+    (dict(num_heads=48), B.PA_ERR_UNSUPPORTED),
+    (dict(page_size=8), B.PA_ERR_UNSUPPORTED),
+    (dict(num_rows=-1), B.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), B.PA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), B.PA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=2 ** 26, page_size=64), B.PA_ERR_UNSUPPORTED),  # reach beyond 2^31
+    (dict(), B.PA_ERR_INVALID_ARG),  # a valid problem with NULL pointers
+])
+def test_mqa_refusals_come_before_the_device(kw, status):
+    st = B.lib().pa_mqa_logits_mxfp4(B.ctypes.byref(_mprob(**kw)), *([None] * 11))
+    assert st == status
+    assert B.pa_last_error()
+
+
+def test_mqa_with_no_rows_is_a_no_op():
+    assert B.lib().pa_mqa_logits_mxfp4(B.ctypes.byref(_mprob(num_rows=0)), *([None] * 11)) == B.PA_OK
+
+
 def test_host_length_checks():
     with pytest.raises(B.PaError):
         B.pa_plan_host(_prob(), [10, -1, 30, 40])
