@@ -49,7 +49,7 @@ METRIC = "KV-read HBM GB/s and % of peak; µs per pa_decode call per config"
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("pa_kernels.hip", "pa_kv_write.hip", "pa_internal.h"):
+    for f in ("pa_kernels.hip", "pa_kv_write.hip", "pa_mqa_logits.hip", "pa_internal.h"):
         with open(os.path.join(ROOT, "paged_attention_decode_token_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -152,6 +152,25 @@ def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
                               "hbm_read_bytes_per_launch": round(rd), "hbm_write_bytes_per_launch": round(wr),
                               "hbm_bytes_per_launch": round(rd + wr), "algorithmic_bytes": alg,
                               "algorithmic_read_bytes": alg_rd}
+        lines.append("| %s | %s | %d | %.4g | %.4g | %.4g | %.4f |" % (
+            spec.name, kernels[spec.name]["kernel"], len(fv), rd, wr, alg, rd / alg_rd))
+    # the MXFP4 MQA logits, when the run included it (bench.py --mqa): its
+    # 16 x 131072-position decode workload is the launch with the largest grid
+    fg, wg = by_grid(fetch_csv, "FETCH_SIZE", "pa_mqa_logits_mxfp4_kernel"), by_grid(write_csv, "WRITE_SIZE",
+                                                                                    "pa_mqa_logits_mxfp4_kernel")
+    if fg and wg:
+        grid = max(fg)
+        fv, wv = fg[grid], wg[grid]
+        rd = sum(fv) / len(fv) * 1024 * f_factor
+        wr = sum(wv) / len(wv) * 1024 * w_factor
+        spec = I.MQA_DECODE_LONG
+        case = I.make_mqa_case(spec)
+        alg = case.bytes_moved()
+        alg_rd = case.window_tokens() * (case.head_dim // 2 + case.head_dim // 32)
+        kernels[spec.name] = {"kernel": "pa_mqa_logits_mxfp4_kernel<%d>" % (spec.num_heads // 16),
+                              "dispatches": len(fv), "hbm_read_bytes_per_launch": round(rd),
+                              "hbm_write_bytes_per_launch": round(wr), "hbm_bytes_per_launch": round(rd + wr),
+                              "algorithmic_bytes": alg, "algorithmic_read_bytes": alg_rd}
         lines.append("| %s | %s | %d | %.4g | %.4g | %.4g | %.4f |" % (
             spec.name, kernels[spec.name]["kernel"], len(fv), rd, wr, alg, rd / alg_rd))
     doc = {"kernel_source": kernel_source_hash(), "fetch_factor": round(f_factor, 4),
@@ -364,7 +383,8 @@ def time_mqa(steps, warmup):
                            "bytes": nbytes, "GBps": round(gbps, 1),
                            "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1),
                            "tflops": round(case.window_tokens() * case.num_heads * case.head_dim * 2 / (us * 1e-6)
-                                           / 1e12, 1)}
+                                           / 1e12, 1),
+                           "traffic": load_traffic(spec.name)}
         print("%-40s %9.2f us  %7.1f GB/s  %5.1f%%  positions %d" % (
             spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, case.window_tokens()), file=sys.stderr, flush=True)
         del args, case, out

@@ -36,7 +36,10 @@ def build(verbose: bool = False) -> str:
     kern = os.path.join(CSRC, "pa_kernels.hip")
     jobs = [(kern, os.path.join(bdir, "pa_kernels.%d.o" % i), ["-DPA_SHARD=%d" % i]) for i in range(4)]
     jobs.append((os.path.join(CSRC, "pa_kv_write.hip"), os.path.join(bdir, "pa_kv_write.o"), []))
-    jobs.append((os.path.join(CSRC, "pa_mqa_logits.hip"), os.path.join(bdir, "pa_mqa_logits.o"), []))
+    # the MQA-logits kernel reads every MFMA result at once: keep the results in
+    # ordinary VGPRs instead of accumulator registers (no per-element copies)
+    jobs.append((os.path.join(CSRC, "pa_mqa_logits.hip"), os.path.join(bdir, "pa_mqa_logits.o"),
+                 ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]))
     jobs.append((os.path.join(CSRC, "pa_api.cpp"), os.path.join(bdir, "pa_api.cpp.o"), []))
     objs = [j[1] for j in jobs]
 

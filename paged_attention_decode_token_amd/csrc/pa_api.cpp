@@ -635,13 +635,13 @@ pa_status pa_mqa_logits_mxfp4(const pa_mqa_problem* problem, const void* q, cons
         return fail(PA_ERR_UNSUPPORTED, "num_heads %d (supported: 16, 32, 64, 128)", p.num_heads);
     if (p.page_size % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", p.page_size);
     const long long reach = (long long)p.max_blocks_per_seq * p.page_size;
-    if (reach > 0x7FFFFFFFLL - 512 || (long long)p.num_blocks * p.page_size > 0x7FFFFFFFLL ||
-        p.out_stride > 0x7FFFFFFF - 512)
+    if (reach > 0x7FFFFFFFLL - 2 * pa::kMqChunkPositions || (long long)p.num_blocks * p.page_size > 0x7FFFFFFFLL ||
+        p.out_stride > 0x7FFFFFFF - 2 * pa::kMqChunkPositions)
         return fail(PA_ERR_UNSUPPORTED, "a table, pool or output row beyond 2^31 positions");
     const long long max_pos = std::min(reach, (long long)p.out_stride);
-    const long long chunks = (max_pos + 255) / 256;
+    const long long chunks = (max_pos + pa::kMqChunkPositions - 1) / pa::kMqChunkPositions;
     if ((long long)p.num_rows * chunks >= (1LL << 31))
-        return fail(PA_ERR_UNSUPPORTED, "num_rows * ceil(positions / 256) exceeds 2^31");
+        return fail(PA_ERR_UNSUPPORTED, "num_rows * ceil(positions / %d) exceeds 2^31", pa::kMqChunkPositions);
     if (p.num_rows == 0 || max_pos == 0) return PA_OK;
     if (!q || !q_scale || !weights || !k_cache || !k_scale || !block_tables || !row_to_batch || !local_starts ||
         !local_ends || !out)

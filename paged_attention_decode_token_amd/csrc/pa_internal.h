@@ -60,8 +60,9 @@ struct KvWriteArgs {
 // Launch the KV write for head_dim 64, 128 or 256 (hipErrorInvalidValue otherwise).
 hipError_t launch_kv_write_mxfp4(int head_dim, const KvWriteArgs& args, hipStream_t stream);
 
-// MXFP4 paged MQA logits (head_dim 128): one workgroup per (256-position
-// chunk, row) work item.
+// MXFP4 paged MQA logits (head_dim 128): one workgroup per (chunk of
+// kMqChunkPositions positions, row) work item.
+constexpr int kMqChunkPositions = 512;
 struct MqaArgs {
     const uint8_t* q;        // [rows][H][64]
     const uint8_t* q_scale;  // [rows][H][4]

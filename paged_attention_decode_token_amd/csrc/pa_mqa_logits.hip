@@ -9,8 +9,13 @@
 // with q and K in MXFP4 (e2m1, one e8m0 scale per 32 elements), head_dim 128.
 // relu keeps a NaN, so a NaN scale reaches the positions that read it.
 //
-// Work: a workgroup takes 256 positions of one row; each wave 64 of them as
-// four 16-token tiles. Per tile and group of 16 heads, one
+// Built with the MFMA results in ordinary VGPRs (-amdgpu-mfma-vgpr-form): the
+// accumulator-register form costs one copy per result element here.
+//
+// Work: a workgroup takes 512 positions of one row; each wave 128 of them as
+// eight 16-token tiles (longer waves, double-buffered or not, measured slower:
+// what pays is many waves with their loads in flight). Per tile and group of
+// 16 heads, one
 // v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 on both sides gives
 // S[head][token]: A = the row's q (16 heads, loaded once per wave), B = the
 // tile's 16 K rows. Lane layouts, measured on gfx950: A lane (m, g) nibble i
@@ -37,14 +42,26 @@ typedef uint32_t mq_u32x4 __attribute__((ext_vector_type(4)));
 
 #define MQ_DEV __device__ __forceinline__
 
-constexpr int kMqChunk = 256;   // positions per workgroup
+constexpr int kMqTiles = 8;              // 16-token tiles per wave
+constexpr int kMqWave = 16 * kMqTiles;   // positions per wave
+constexpr int kMqChunk = 4 * kMqWave;    // positions per workgroup (four waves)
+static_assert(kMqChunk == kMqChunkPositions, "the host sizes the grid by kMqChunkPositions");
 constexpr uint32_t kMqXcds = 8;  // accelerator complex dies of an MI355X
 
 MQ_DEV uint32_t mq_div(uint32_t x, int32_t d, int32_t shift) {
     return shift >= 0 ? x >> shift : x / (uint32_t)d;
 }
 
-// HT groups of 16 heads; head_dim 128 (one MFMA per group and tile).
+// relu on the bits: the integer max with 0 keeps every non-negative float and
+// turns negatives and -0 into +0 (one v_max_i32).
+MQ_DEV float mq_relu(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
+// HT groups of 16 heads; head_dim 128 (one MFMA per group and tile). A wave
+// owns kMqTiles 16-token tiles: it reads the block-table columns they span
+// once (one per lane) and hands each tile its page id by a lane shuffle, then
+// issues every tile's K load before the first MFMA, so no load waits on another.
 template <int HT>
 __global__ __launch_bounds__(256) void pa_mqa_logits_mxfp4_kernel(const MqaArgs a) {
     // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -59,27 +76,32 @@ __global__ __launch_bounds__(256) void pa_mqa_logits_mxfp4_kernel(const MqaArgs 
     if (b < 0 || b >= a.num_seqs) return;
     const int t0 = max(a.local_starts[r], 0);
     const int t1 = min(a.local_ends[r], a.max_pos);
-    const int c0 = chunk * kMqChunk;
-    if (c0 >= t1 || c0 + kMqChunk <= t0) return;
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int ws = chunk * kMqChunk + kMqWave * wave;  // this wave's first position
+    if (ws >= t1 || ws + kMqWave <= t0) return;        // the whole wave, uniformly
+
     const int n = lane & 15, g = lane >> 4;
     const int H = HT * 16;
 
-    // this wave's four tiles: page ids, then K rows and scale bytes
-    const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-    mq_u32x4 kd[4];
-    uint32_t ks[4];
+    // page ids of the columns the wave's positions span (at most
+    // kMqWave / 16 + 1 of them): lane l holds column cb + l, clamped into the
+    // table, its entry clamped into the pool
+    const uint32_t cb = mq_div((uint32_t)ws, a.page_size, a.page_shift);
+    const int32_t* btab = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+    const uint32_t mycol = min(cb + (uint32_t)lane, (uint32_t)(a.max_blocks_per_seq - 1));
+    const int mypage = min(max(btab[mycol], 0), a.num_blocks - 1);
+
+    mq_u32x4 kd[kMqTiles];
+    uint32_t ks[kMqTiles];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        // positions past the window (up to 255 beyond it) are computed and not
-        // stored: their table column and page id are clamped into range
-        const uint32_t t = (uint32_t)(c0 + 64 * wave + 16 * j + n);
+    for (int j = 0; j < kMqTiles; ++j) {
+        // positions past the window (at most to the end of the wave's range)
+        // are computed and not stored
+        const uint32_t t = (uint32_t)(ws + 16 * j + n);
         const uint32_t colt = mq_div(t, a.page_size, a.page_shift);
         const uint32_t slot = t - colt * (uint32_t)a.page_size;
-        const uint32_t col = min(colt, (uint32_t)(a.max_blocks_per_seq - 1));
-        const int page = min(max(bt[col], 0), a.num_blocks - 1);
+        const int page = __shfl(mypage, (int)(colt - cb));  // colt - cb <= kMqWave / 16 < 64
         const size_t krow = (size_t)page * a.page_size + slot;
         kd[j] = *reinterpret_cast<const mq_u32x4*>(a.k_cache + krow * 64 + 16 * g);
         ks[j] = a.k_scale[krow * 4 + g];
@@ -96,25 +118,40 @@ __global__ __launch_bounds__(256) void pa_mqa_logits_mxfp4_kernel(const MqaArgs 
         qs[i] = a.q_scale[qrow * 4 + g];
         w[i] = *reinterpret_cast<const mq_f32x4*>(a.weights + (size_t)r * H + 16 * i + 4 * g);
     }
+    // NaN reaches a score only through an e8m0 NaN scale (0xFF; e2m1 has no
+    // NaN): a q scale makes every score of the row NaN, a K scale every score
+    // of its token. Both are read off the scale bytes, so relu may turn a NaN
+    // into 0. Scores are assumed to stay within fp32 range.
+    bool qbad = false;
+#pragma unroll
+    for (int i = 0; i < HT; ++i) qbad |= qs[i] == 0xFFu;
+    const bool row_nan = __any(qbad);
+    const float qnan = __builtin_nanf("");
+    float* orow = a.out + (size_t)r * a.out_stride;
 
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kMqTiles; ++j) {
         const mq_i32x8 kb = {(int)kd[j].x, (int)kd[j].y, (int)kd[j].z, (int)kd[j].w, 0, 0, 0, 0};
-        float acc = 0.f;
+        mq_f32x4 s[HT];
 #pragma unroll
         for (int i = 0; i < HT; ++i) {
             const mq_i32x8 qa = {(int)qd[i].x, (int)qd[i].y, (int)qd[i].z, (int)qd[i].w, 0, 0, 0, 0};
-            mq_f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, kb, s, 4, 4, 0, (int)qs[i], 0, (int)ks[j]);
-            acc += w[i].x * (s.x < 0.f ? 0.f : s.x);
-            acc += w[i].y * (s.y < 0.f ? 0.f : s.y);
-            acc += w[i].z * (s.z < 0.f ? 0.f : s.z);
-            acc += w[i].w * (s.w < 0.f ? 0.f : s.w);
+            const mq_f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            s[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, kb, z, 4, 4, 0, (int)qs[i], 0, (int)ks[j]);
+        }
+        float acc = ks[j] == 0xFFu ? qnan : 0.f;
+#pragma unroll
+        for (int i = 0; i < HT; ++i) {
+            acc += w[i].x * mq_relu(s[i].x);
+            acc += w[i].y * mq_relu(s[i].y);
+            acc += w[i].z * mq_relu(s[i].z);
+            acc += w[i].w * mq_relu(s[i].w);
         }
         acc += __shfl_xor(acc, 16);
         acc += __shfl_xor(acc, 32);
-        const int t = c0 + 64 * wave + 16 * j + n;
-        if (g == 0 && t >= t0 && t < t1) a.out[(size_t)r * a.out_stride + t] = acc;
+        if (row_nan) acc = qnan;
+        const int t = ws + 16 * j + n;
+        if (g == 0 && t >= t0 && t < t1) orow[t] = acc;
     }
 }
 
