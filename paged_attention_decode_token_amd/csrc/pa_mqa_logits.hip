@@ -84,6 +84,19 @@ __global__ __launch_bounds__(256) void pa_mqa_logits_mxfp4_kernel(const MqaArgs 
     const int n = lane & 15, g = lane >> 4;
     const int H = HT * 16;
 
+    // the row's q fragments (head 16i + n, block g) and the weights of the
+    // heads this lane's accumulator rows hold (16i + 4g + 0..3), issued first:
+    // they depend on the row only, and overlap the block-table read
+    mq_u32x4 qd[HT];
+    uint32_t qs[HT];
+    mq_f32x4 w[HT];
+#pragma unroll
+    for (int i = 0; i < HT; ++i) {
+        const size_t qrow = (size_t)r * H + 16 * i + n;
+        qd[i] = *reinterpret_cast<const mq_u32x4*>(a.q + qrow * 64 + 16 * g);
+        qs[i] = a.q_scale[qrow * 4 + g];
+        w[i] = *reinterpret_cast<const mq_f32x4*>(a.weights + (size_t)r * H + 16 * i + 4 * g);
+    }
     // page ids of the columns the wave's positions span (at most
     // kMqWave / 16 + 1 of them): lane l holds column cb + l, clamped into the
     // table, its entry clamped into the pool
@@ -105,18 +118,6 @@ __global__ __launch_bounds__(256) void pa_mqa_logits_mxfp4_kernel(const MqaArgs 
         const size_t krow = (size_t)page * a.page_size + slot;
         kd[j] = *reinterpret_cast<const mq_u32x4*>(a.k_cache + krow * 64 + 16 * g);
         ks[j] = a.k_scale[krow * 4 + g];
-    }
-    // the row's q fragments (head 16i + n, block g) and the weights of the
-    // heads this lane's accumulator rows hold (16i + 4g + 0..3)
-    mq_u32x4 qd[HT];
-    uint32_t qs[HT];
-    mq_f32x4 w[HT];
-#pragma unroll
-    for (int i = 0; i < HT; ++i) {
-        const size_t qrow = (size_t)r * H + 16 * i + n;
-        qd[i] = *reinterpret_cast<const mq_u32x4*>(a.q + qrow * 64 + 16 * g);
-        qs[i] = a.q_scale[qrow * 4 + g];
-        w[i] = *reinterpret_cast<const mq_f32x4*>(a.weights + (size_t)r * H + 16 * i + 4 * g);
     }
     // NaN reaches a score only through an e8m0 NaN scale (0xFF; e2m1 has no
     // NaN): a q scale makes every score of the row NaN, a K scale every score
