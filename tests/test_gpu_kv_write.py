@@ -58,6 +58,8 @@ SMALL_WRITE = [I.small_write(s) for s in I.WRITE_FULL] + [
                                               seed=8),
     I.small_write(I.MXFP4_WRITE_FILL).replace(name="d128_p128_h8_ragged", num_kv_heads=8, num_seqs=4,
                                               lens=("fixed", (129, 1, 255, 640)), pad_tokens=3, seed=9),
+    # a page size that is not a power of two takes the division path for the slot
+    I.small_write(I.MXFP4_WRITE_FILL).replace(name="d128_p48_h4", num_kv_heads=4, page_size=48, seed=10),
 ]
 
 
