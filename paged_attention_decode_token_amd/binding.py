@@ -204,13 +204,41 @@ def _dev(t, name, nullable=False):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def pa_decode(plan: Plan, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, out,
-              stream=None):
-    """Enqueue one decode on `stream` (torch's current stream by default)."""
+def _check_decode_sizes(p: pa_problem, query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                        context_lens, out):
+    """The C ABI sees only pointers: check here that every tensor holds exactly
+    the bytes the problem implies for its format and layout."""
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
     if out.dtype != torch.bfloat16:
         raise ValueError("out must be bfloat16")
+    B, QL, H, D, PG, NB = p.num_seqs, p.qlen, p.num_kv_heads, p.head_dim, p.page_size, p.num_blocks
+    Hq = H * p.q_per_kv
+    row = {PA_KV_BF16: 2 * D, PA_KV_FP8_E4M3: D, PA_KV_MXFP4: D // 2}[p.kv_dtype]
+    need = [(query, "query", B * QL * Hq * D * (1 if p.q_dtype == PA_Q_FP8_E4M3 else 2)),
+            (key_cache, "key_cache", NB * H * PG * row), (value_cache, "value_cache", NB * H * PG * row),
+            (out, "out", B * QL * Hq * D * 2), (context_lens, "context_lens", B * 4)]
+    if p.kv_dtype == PA_KV_MXFP4:
+        need += [(k_scale, "k_scale", NB * H * PG * (D // 32)), (v_scale, "v_scale", NB * H * PG * (D // 32))]
+    elif p.scale_mode == PA_SCALE_PER_TOKEN:
+        need += [(k_scale, "k_scale", NB * H * PG * 4), (v_scale, "v_scale", NB * H * PG * 4)]
+    elif p.scale_mode == PA_SCALE_PER_TENSOR:
+        need += [(k_scale, "k_scale", 4), (v_scale, "v_scale", 4)]
+    for t, name, nbytes in need:
+        if t is None:
+            raise ValueError("%s is required" % name)
+        if t.numel() * t.element_size() != nbytes:
+            raise ValueError("%s holds %d bytes, the problem needs %d" % (name, t.numel() * t.element_size(), nbytes))
+    if tuple(block_tables.shape) != (B, p.max_blocks_per_seq):
+        raise ValueError("block_tables has shape %s, the problem needs %s" % (
+            tuple(block_tables.shape), (B, p.max_blocks_per_seq)))
+
+
+def pa_decode(plan: Plan, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, out,
+              stream=None):
+    """Enqueue one decode on `stream` (torch's current stream by default)."""
+    _check_decode_sizes(plan.problem, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens,
+                        out)
     st = lib().pa_decode(ctypes.c_void_p(plan.ptr), _dev(query, "query"), _dev(key_cache, "key_cache"),
                          _dev(value_cache, "value_cache"), _dev(k_scale, "k_scale", True),
                          _dev(v_scale, "v_scale", True), _dev(block_tables, "block_tables"),
@@ -223,10 +251,7 @@ def pa_decode(plan: Plan, query, key_cache, value_cache, k_scale, v_scale, block
 def pa_decode_direct(problem: pa_problem, query, key_cache, value_cache, k_scale, v_scale, block_tables,
                      context_lens, out, stream=None):
     """Plan-free decode (one task per sequence and KV head); enqueued on `stream`."""
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
-    if out.dtype != torch.bfloat16:
-        raise ValueError("out must be bfloat16")
+    _check_decode_sizes(problem, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, out)
     st = lib().pa_decode_direct(ctypes.byref(problem), _dev(query, "query"), _dev(key_cache, "key_cache"),
                                 _dev(value_cache, "value_cache"), _dev(k_scale, "k_scale", True),
                                 _dev(v_scale, "v_scale", True), _dev(block_tables, "block_tables"),
@@ -310,14 +335,28 @@ def mqa_problem_of(case) -> pa_mqa_problem:
 
 def pa_mqa_logits_mxfp4(problem: pa_mqa_problem, q, q_scale, weights, k_cache, k_scale, block_tables, row_to_batch,
                         local_starts, local_ends, out, stream=None):
-    """Enqueue the MXFP4 paged MQA logits on `stream`; writes only window positions of `out`."""
-    for t, name, dt in ((q, "q", torch.uint8), (q_scale, "q_scale", torch.uint8), (weights, "weights", torch.float32),
-                        (k_cache, "k_cache", torch.uint8), (k_scale, "k_scale", torch.uint8),
-                        (block_tables, "block_tables", torch.int32), (row_to_batch, "row_to_batch", torch.int32),
-                        (local_starts, "local_starts", torch.int32), (local_ends, "local_ends", torch.int32),
-                        (out, "out", torch.float32)):
+    """Enqueue the MXFP4 paged MQA logits on `stream`; writes only window positions of `out`.
+
+    The tensors must have the shapes `problem` describes (checked here, since the
+    C ABI sees only pointers): q [R, H, D/2], q_scale [R, H, D/32], weights [R, H],
+    k_cache [NB, PG, D/2], k_scale [NB, PG, D/32], block_tables [B, W],
+    row_to_batch / local_starts / local_ends [R], out [R, out_stride]."""
+    p = problem
+    R, H, D, NB, PG = p.num_rows, p.num_heads, p.head_dim, p.num_blocks, p.page_size
+    for t, name, dt, shape in ((q, "q", torch.uint8, (R, H, D // 2)),
+                               (q_scale, "q_scale", torch.uint8, (R, H, D // 32)),
+                               (weights, "weights", torch.float32, (R, H)),
+                               (k_cache, "k_cache", torch.uint8, (NB, PG, D // 2)),
+                               (k_scale, "k_scale", torch.uint8, (NB, PG, D // 32)),
+                               (block_tables, "block_tables", torch.int32, (p.num_seqs, p.max_blocks_per_seq)),
+                               (row_to_batch, "row_to_batch", torch.int32, (R,)),
+                               (local_starts, "local_starts", torch.int32, (R,)),
+                               (local_ends, "local_ends", torch.int32, (R,)),
+                               (out, "out", torch.float32, (R, p.out_stride))):
         if t.dtype != dt:
             raise ValueError("%s must be %s" % (name, dt))
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, the problem needs %s" % (name, tuple(t.shape), shape))
     st = lib().pa_mqa_logits_mxfp4(ctypes.byref(problem), _dev(q, "q"), _dev(q_scale, "q_scale"),
                                    _dev(weights, "weights"), _dev(k_cache, "k_cache"), _dev(k_scale, "k_scale"),
                                    _dev(block_tables, "block_tables"), _dev(row_to_batch, "row_to_batch"),

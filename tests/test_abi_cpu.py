@@ -134,6 +134,42 @@ def test_mqa_with_no_rows_is_a_no_op():
     assert B.lib().pa_mqa_logits_mxfp4(B.ctypes.byref(_mprob(num_rows=0)), *([None] * 11)) == B.PA_OK
 
 
+def test_mqa_binding_checks_shapes_before_the_device():
+    from paged_attention_decode_token_amd import inputs as MI
+    case = MI.make_mqa_case(MI.small_mqa(MI.MQA_DECODE_LONG))
+    prob = B.mqa_problem_of(case)
+    out = torch.zeros((case.num_rows, case.out_stride), dtype=torch.float32)
+    args = [case.q, case.q_scale, case.weights, case.k_cache, case.k_scale, case.block_tables, case.row_to_batch,
+            case.local_starts, case.local_ends, out]
+    for i, bad in ((0, case.q[:, :, :32]), (2, case.weights[:-1]), (5, case.block_tables[:, :-1]),
+                   (9, out[:, :-16])):
+        a = list(args)
+        a[i] = bad.contiguous()
+        with pytest.raises(ValueError, match="shape"):
+            B.pa_mqa_logits_mxfp4(prob, *a)
+    with pytest.raises(ValueError, match="device"):  # right shapes, host tensors
+        B.pa_mqa_logits_mxfp4(prob, *args)
+
+
+@pytest.mark.parametrize("spec", [I.TINY_BF16, I.small(I.FP8TOK_Q1), I.small(I.FP8_TRANS), I.small(I.MXFP4_SHORT_Q8)],
+                         ids=lambda s: s.name)
+def test_decode_binding_checks_sizes_before_the_device(spec):
+    case = I.make_case(spec)
+    prob = B.problem_of(case)
+    t = case.tensors()
+    out = torch.zeros((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), dtype=torch.bfloat16)
+    args = dict(query=t["query"], key_cache=t["key_cache"], value_cache=t["value_cache"], k_scale=t["k_scale"],
+                v_scale=t["v_scale"], block_tables=t["block_tables"], context_lens=t["context_lens"], out=out)
+    for name, bad in (("key_cache", t["key_cache"][:-1]), ("block_tables", t["block_tables"][:, :-1]),
+                      ("out", out[:-1]), ("query", t["query"][:, :, :-1])):
+        a = dict(args)
+        a[name] = bad.contiguous()
+        with pytest.raises(ValueError, match="bytes|shape"):
+            B.pa_decode_direct(prob, **a)
+    with pytest.raises(ValueError, match="device"):  # right sizes, host tensors
+        B.pa_decode_direct(prob, **args)
+
+
 def test_host_length_checks():
     with pytest.raises(B.PaError):
         B.pa_plan_host(_prob(), [10, -1, 30, 40])
