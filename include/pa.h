@@ -277,7 +277,10 @@ pa_status pa_write_kv_mxfp4(const pa_kv_write_problem* problem, const void* key,
  * head_dim must be 128, num_heads 16, 32, 64 or 128, page_size a multiple of 16.
  * Block-table entries are clamped into [0, num_blocks), so a bad table cannot
  * fault. The result is fp32; each score is a sum of num_heads weighted products,
- * rounded in fp32. Enqueued on `stream`; nothing is allocated or synchronized.
+ * rounded in fp32. A NaN score comes only from an e8m0 NaN scale byte (0xFF) in
+ * the row's q or the position's K row, and such a score is NaN exactly as relu
+ * keeps it; scores whose partial sums leave the fp32 range are not specified.
+ * Enqueued on `stream`; nothing is allocated or synchronized.
  */
 typedef struct pa_mqa_problem {
     int32_t num_rows;
