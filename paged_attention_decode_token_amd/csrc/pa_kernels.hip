@@ -202,13 +202,27 @@ struct Cfg {
     // against 183-209 us on the batch-64 workload).
     static constexpr bool VDMA = !VT && KV != KV_MXFP4 && NT_ == 1 && !(KV_ == KV_BF16 && PG_ == 128);
     static constexpr bool STAGE_V = !VT && !VDMA;
+    // Whole-stage prefetch (fp8 caches with per-token scales on the LDS-DMA
+    // path, one workgroup per CU): the K, V and scale loads of a wave's next
+    // slice are all issued at the top of the current one, into a second K
+    // register set, a second V tile and a second scale block (the scales also
+    // arrive by LDS DMA). One full wait per slice then covers exactly the
+    // slice about to be computed, so a slice costs max(load latency, compute)
+    // rather than their sum: with K in one register set, the next slice's K
+    // can only be issued after this slice's QK has read it. (The compiler waits
+    // for everything outstanding before using a register loaded ahead of an
+    // LDS DMA, so register loads cannot be kept in flight across a DMA wait;
+    // hence the one full wait at the top.)
+    static constexpr bool PF = VDMA && KV_ == KV_FP8 && SC_ == SC_TOKEN;
     static constexpr int VPITCH = D * 2 + 16;                        // staged bf16 row pitch in bytes
     static constexpr int CPR = ROWB / 16;                            // 16-byte chunks per V row (DMA)
     static constexpr int VSTAGE_BYTES = VDMA ? 64 * ROWB : (STAGE_V ? 32 * VPITCH : 0);  // per wave
+    static constexpr int SCALE_BYTES = PF ? 512 : 0;                 // K then V scales of 64 tokens (fp32)
+    static constexpr int WAVE_LDS = (PF ? 2 : 1) * (VSTAGE_BYTES + SCALE_BYTES);  // per wave
     static constexpr int ROWS_PAD = 16 * NT;
     static constexpr int OPITCH = D + 4;                             // floats
     static constexpr int EPI_BYTES = 2 * ROWS_PAD * OPITCH * 4 + 2 * 4 * ROWS_PAD * 4;
-    static constexpr int SMEM = (4 * VSTAGE_BYTES > EPI_BYTES) ? 4 * VSTAGE_BYTES : EPI_BYTES;
+    static constexpr int SMEM = (4 * WAVE_LDS > EPI_BYTES) ? 4 * WAVE_LDS : EPI_BYTES;
     // staging geometry for token-major V loads
     static constexpr int LPR = ROWB / 16;         // lanes per token row
     static constexpr int TPI = 64 / LPR;          // tokens per load instruction
@@ -478,7 +492,7 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
 #pragma unroll
         for (int c = 0; c < 4; ++c) kb.ksc[c] = ld4_kv(srow + 4 * c * C::SROWB);  // byte lg is used
     }
-    if constexpr (C::SC == SC_TOKEN) {
+    if constexpr (C::SC == SC_TOKEN && !C::PF) {
         const long off = ((long)sp.tpage * a.num_kv_heads * PG + slot_in_page(sp, 16 * lg)) * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -493,6 +507,49 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
             }
         }
     }
+}
+
+// Whole-stage prefetch: per-token K and V scales of the slice by LDS DMA. Lane
+// l fetches those of slice token l, which land at bytes [4l, 4l + 4) of the
+// K half (slds) and of the V half (slds + 256). Scales of heads that share a
+// page lie in one line, so the loads are not nontemporal.
+template <class C>
+PA_DEV void load_scales_dma(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, char* slds) {
+    const int l = cx.lane;
+    // several pages per slice only with 16-token pages, where token l lies in
+    // this lane's score page (tokens 16 lg + [0, 16))
+    static_assert(C::NPC == 1 || C::PG == 16, "page of token l");
+    const int pg = C::NPC == 1 ? sp.pg[0] : sp.tpage;
+    const long off = ((long)pg * a.num_kv_heads * C::PG + slot_in_page(sp, l)) * 4;
+    __builtin_amdgcn_global_load_lds((const void*)(cx.ksbase + off), (__attribute__((address_space(3))) void*)(slds),
+                                     4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(cx.vsbase + off),
+                                     (__attribute__((address_space(3))) void*)(slds + 256), 4, 0, 0);
+}
+
+// This lane's 16 K and V scales (slice tokens 16 lg + [0, 16)) from the scale
+// block of a landed slice. slds is restrict-qualified: the next slice's DMA is
+// in flight into the other block, and the full wait at the top of the slice
+// already covers this one.
+template <class C>
+PA_DEV void read_scales_lds(const Ctx& cx, const char* __restrict__ slds, KBuf<C>& kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(slds + 64 * cx.lg + 16 * i);
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(slds + 256 + 64 * cx.lg + 16 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            kb.tks[4 * i + j] = k4[j];
+            kb.tvs[4 * i + j] = v4[j];
+        }
+    }
+}
+
+// Whole-stage prefetch: wait until every load issued so far has landed.
+PA_DEV void full_wait() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Before a slice's V DMA: wait for everything outstanding (this slice's K).
@@ -703,7 +760,7 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
                 }
         }
     }
-    if constexpr (C::VDMA) {
+    if constexpr (C::VDMA && !C::PF) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_AFTER));  // this slice's V is in LDS
         __builtin_amdgcn_sched_barrier(0);
@@ -901,7 +958,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
         for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    char* vlds = smem + cx.wave * C::VSTAGE_BYTES;
+    char* vlds = smem + cx.wave * C::WAVE_LDS;
 
     // Query row r of this lane (query token i = r / G) attends to
     // [row_s, row_e): e = L - qlen + i + 1 when causal, else L; s = e - window
@@ -936,7 +993,58 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     const int T1 = te;
     const int F0 = max(T0, (s_max + kTileTokens - 1) / kTileTokens);
     const int F1 = max(F0, min(T1, e_min / kTileTokens));
-    if (T1 > T0) {
+    if constexpr (C::PF) {
+        if (T1 > T0) {
+            // stage = K (registers), V tile and scale block (LDS) of one slice;
+            // stage(tile + 1) is issued right after the wait for stage(tile)
+            using Masked = BoolTag<true>;
+            using Full = BoolTag<false>;
+            constexpr int BUF = C::VSTAGE_BYTES + C::SCALE_BYTES;
+            int cb = T0 * kTileTokens + 64 * cx.wave;
+            PageCache<C> pc;
+            page_cache_fill<C>(a, cx, pc, T0);
+            SlicePages<C> sp = slice_pages<C>(a, cx, pc, T0);
+            char* vcur = vlds;
+            char* vnext = vlds + BUF;
+            KBuf<C> kcur, knext;
+            VBuf<C> vb;
+            load_v<C>(a, cx, sp, vb, vcur);
+            load_scales_dma<C>(a, cx, sp, vcur + C::VSTAGE_BYTES);
+            load_k<C>(a, cx, sp, knext);
+            int tile = T0;
+            auto step = [&](auto mask_tag) {
+                constexpr bool M = decltype(mask_tag)::value;
+                full_wait();
+                kcur = knext;
+                sp = slice_pages<C>(a, cx, pc, tile + 1);
+                load_v<C>(a, cx, sp, vb, vnext);
+                load_scales_dma<C>(a, cx, sp, vnext + C::VSTAGE_BYTES);
+                load_k<C>(a, cx, sp, knext);
+                // the whole next stage is issued before this slice computes
+                __builtin_amdgcn_sched_barrier(0);
+                read_scales_lds<C>(cx, vcur + C::VSTAGE_BYTES, kcur);
+                PFrag<C> pf;
+                qk_softmax<C, M>(a, cx, qf, kcur, st, pf, cb);
+                pv<C, M, 0>(cx, vb, pf, st, cb, vcur);
+                char* t = vcur;
+                vcur = vnext;
+                vnext = t;
+                cb += kTileTokens;
+                ++tile;
+            };
+            if constexpr (C::WIN)
+                for (; tile < F0 && tile + 1 < T1;) step(Masked{});
+            for (; tile < F1 && tile + 1 < T1;) step(Full{});
+            if constexpr (C::WIN)
+                for (; tile + 1 < T1;) step(Masked{});
+            full_wait();
+            kcur = knext;
+            read_scales_lds<C>(cx, vcur + C::VSTAGE_BYTES, kcur);
+            PFrag<C> pf;
+            qk_softmax<C, true>(a, cx, qf, kcur, st, pf, cb);
+            pv<C, true, 0>(cx, vb, pf, st, cb, vcur);
+        }
+    } else if (T1 > T0) {
         int cb = T0 * kTileTokens + 64 * cx.wave;
         PageCache<C> pc;
         page_cache_fill<C>(a, cx, pc, T0);

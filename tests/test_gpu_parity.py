@@ -239,6 +239,12 @@ GPU_MASK_SPECS = [
     I.Spec("g_bf16_p128_w256", 3, ("fixed", (255, 256, 2049)), 1, 2, 8, 128, 128, "bf16", seed=46, window=256),
     I.Spec("g_bf16_q4_g8_causal_win", 3, ("fixed", (3, 511, 1300)), 4, 1, 8, 128, 64, "bf16", seed=47, causal=1,
            window=257),
+    # fp8 per-token caches with 16 query rows, head_dim 128 and 256, pages of
+    # 64 and 128 tokens: the whole-stage-prefetch instances
+    I.Spec("g_fp8tok_d128_p64_win", 3, ("fixed", (65, 700, 2100)), 1, 2, 8, 128, 64, "fp8", "token", seed=48,
+           window=600),
+    I.Spec("g_fp8tok_d256_p128_q2_causal", 3, ("fixed", (1, 383, 1800)), 2, 1, 8, 256, 128, "fp8", "token",
+           seed=49, causal=1),
 ]
 
 
