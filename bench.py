@@ -126,8 +126,10 @@ def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
     kernels = {}
     lines = ["| workload | tile kernel | dispatches | HBM read B/launch | HBM write B/launch | algorithmic B | read / algorithmic |",
              "|---|---|---|---|---|---|---|"]
-    for spec in (I.BF16_P64, I.BF16_P128):
+    for spec in (I.BF16_P64, I.BF16_P128, I.FP8TOK_Q1, I.FP8TOK_Q4):
         tag = kernel_tag_of(spec)
+        if spec.kv_dtype != "bf16" and not any(tag in k for k in fetch):
+            continue  # the fp8 rows only when the run included them (--all --workloads ...)
         fv, wv = one(fetch, tag), one(write, tag)
         rd = sum(fv) / len(fv) * 1024 * f_factor
         wr = sum(wv) / len(wv) * 1024 * w_factor
@@ -218,9 +220,14 @@ def time_cpu_oracle(case, target_s=15.0):
                 n, case.num_seqs, reps, nbytes / 1e6, dt)}
 
 
-def time_all(steps, warmup):
+def time_all(steps, warmup, names=None):
     """Per workload: cold-cache median us per pa_decode call, and the tile / merge
-    kernel split from the library's events (inputs resident in HBM)."""
+    kernel split from the library's events (inputs resident in HBM).
+
+    Each event pair also brackets the event packets' own queue time (a few us,
+    which is a tenth of a 60 us call). So a second, differential figure is taken
+    too: `steps` cold calls (flush, call, flush, call, ...) between two events,
+    minus `steps` flushes alone between two events, divided by `steps`."""
     import statistics
 
     import torch
@@ -231,7 +238,8 @@ def time_all(steps, warmup):
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB last-level cache
     flush_out = torch.empty((), dtype=torch.float32, device="cuda")
     rows = {}
-    for spec in I.FULL:
+    specs = I.FULL if not names else [I.BY_NAME[n] for n in names]
+    for spec in specs:
         case = I.make_case(spec)
         d = pa.device_tensors(case)
         plan = pa.pa_plan(pa.problem_of(case), case.context_lens)
@@ -252,6 +260,21 @@ def time_all(steps, warmup):
             b.record()
         torch.cuda.synchronize()
         us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+        # differential cold time: the event packets' cost is paid once per batch
+        a, b = ev[0]
+        a.record()
+        for _ in range(steps):
+            torch.amax(flush, dim=0, out=flush_out)
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        t_calls = a.elapsed_time(b)
+        a.record()
+        for _ in range(steps):
+            torch.amax(flush, dim=0, out=flush_out)
+        b.record()
+        torch.cuda.synchronize()
+        us_diff = (t_calls - a.elapsed_time(b)) * 1e3 / steps
         prob = pa.problem_of(case)
 
         def call_direct():
@@ -276,16 +299,19 @@ def time_all(steps, warmup):
         nbytes = read_bytes(case)
         inf = plan.info()
         gbps = nbytes / (us * 1e-6) / 1e9
-        rows[spec.name] = {"us_per_call": round(us, 2), "tile_us": round(t_ms / n * 1e3, 2),
+        rows[spec.name] = {"us_per_call": round(us, 2), "us_per_call_differential": round(us_diff, 2),
+                           "pct_of_hbm_peak_differential": round(100 * nbytes / (us_diff * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                           "tile_us": round(t_ms / n * 1e3, 2),
                            "merge_us": round(m_ms / n * 1e3, 2) if inf.merge_needed else 0.0,
                            "kv_bytes": nbytes, "kv_GBps": round(gbps, 1),
                            "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1),
                            "tasks": inf.num_tasks, "slots": inf.slots, "partitions_max": inf.max_parts,
                            "plan_free_us_per_call": round(us_direct, 2),
                            "plan_free_pct_of_hbm_peak": round(100 * nbytes / (us_direct * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
-        print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  tile %8.2f us  tasks %5d slots %4d  plan-free %8.2f us" % (
-            spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, t_ms / n * 1e3, inf.num_tasks, inf.slots, us_direct),
-            file=sys.stderr, flush=True)
+        print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  differential %8.2f us %5.1f%%  tile %8.2f us  tasks %5d slots %4d  "
+              "plan-free %8.2f us" % (spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, us_diff,
+                                      100 * nbytes / (us_diff * 1e-6) / 1e9 / HBM_PEAK_GBS, t_ms / n * 1e3,
+                                      inf.num_tasks, inf.slots, us_direct), file=sys.stderr, flush=True)
         del d, plan, out, case
         torch.cuda.empty_cache()
     return rows
@@ -404,6 +430,8 @@ def main():
                     help="also time the MXFP4 cache-write workloads (implied by --all)")
     ap.add_argument("--mqa", action="store_true",
                     help="also time the MXFP4 paged MQA-logits workloads (implied by --all)")
+    ap.add_argument("--workloads", default="",
+                    help="with --all: comma-separated workload names to time (default: every workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -518,7 +546,8 @@ def main():
         del variants
         torch.cuda.empty_cache()
     if args.all:
-        res["all_workloads"] = time_all(args.steps, args.warmup)
+        res["all_workloads"] = time_all(args.steps, args.warmup,
+                                        [w for w in args.workloads.split(",") if w] or None)
     if args.all or args.kv_write:
         res["kv_write"] = time_writes(args.steps, args.warmup)
     if args.all or args.mqa:
