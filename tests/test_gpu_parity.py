@@ -114,7 +114,7 @@ def test_plan_variants_agree_with_oracle(spec, variant):
 EDGE_LENS = (0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 767, 1000)
 
 
-@pytest.mark.parametrize("base", [I.TINY_BF16, I.BF16_P64, I.FP8TOK_Q4, I.FP8_TRANS, I.MXFP4_SHORT_QBF],
+@pytest.mark.parametrize("base", [I.TINY_BF16, I.BF16_P64, I.FP8TOK_Q1, I.FP8TOK_Q4, I.FP8_TRANS, I.MXFP4_SHORT_QBF],
                          ids=lambda s: s.name)
 def test_edge_lengths(base):
     spec = base.replace(name=base.name + "_edges", num_seqs=len(EDGE_LENS), lens=("fixed", EDGE_LENS),
@@ -202,7 +202,7 @@ def test_plan_free_equals_one_partition_plan_and_oracle(spec):
     check_parity(direct, oracle.pa_decode(case), what=spec.name + " plan-free")
 
 
-@pytest.mark.parametrize("base", [I.TINY_BF16, I.BF16_P64, I.FP8TOK_Q4, I.FP8_TRANS, I.MXFP4_SHORT_QBF],
+@pytest.mark.parametrize("base", [I.TINY_BF16, I.BF16_P64, I.FP8TOK_Q1, I.FP8TOK_Q4, I.FP8_TRANS, I.MXFP4_SHORT_QBF],
                          ids=lambda s: s.name)
 def test_plan_free_edge_lengths_and_poison(base):
     spec = base.replace(name=base.name + "_edges", num_seqs=len(EDGE_LENS), lens=("fixed", EDGE_LENS),
