@@ -195,12 +195,26 @@ struct Cfg {
     // wave-private LDS tile (64 token rows, XOR-swizzled 16-byte chunks) by
     // LDS DMA and is read back transposed; MXFP4 V is widened to bf16 in
     // registers and staged through LDS one 32-token PV step at a time.
-    // Measured per configuration: one N tile only (with 32 query rows the D 256
-    // kernel spills, and the spill traffic shares the vmcnt the DMA wait
-    // counts on), and not for bf16 pages of 128 tokens (there the register
-    // path at one workgroup per CU beats the DMA path at one or two: 179.5
-    // against 183-209 us on the batch-64 workload).
-    static constexpr bool VDMA = !VT && KV != KV_MXFP4 && NT_ == 1 && !(KV_ == KV_BF16 && PG_ == 128);
+    // Measured per configuration: one N tile (32 query rows only in the fp8
+    // per-token case below), and not for bf16 pages of 128 tokens (there the
+    // register path at one workgroup per CU beats the DMA path at one or two:
+    // 179.5 against 183-209 us on the batch-64 workload).
+    //
+    // The wait before PV allows the KVMEM loads issued after the slice's DMA to
+    // be outstanding. Loads, the DMA included, complete in issue order, and any
+    // other memory operation issued after the DMA (a spill) only adds to the
+    // outstanding count, so the wait stays sufficient with spills; they cost
+    // time, not correctness.
+    //
+    // fp8 per-token caches with 32 query rows at head_dim 256 take the DMA path
+    // (with the query fragments in LDS, which keeps the loop free of spills)
+    // wherever the register-staged loop spills to scratch: in the windowed
+    // instances and at page 64, where each scratch reload in the loop waits for
+    // every load in flight (qlen 4, batch 16: 82-87 against 90-118 us per call).
+    // The plain page-16 and page-128 instances keep register staging, whose
+    // loops do not spill and which measured faster there (80-81 against 99 us).
+    static constexpr bool NT2_DMA = KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 2 && D_ == 256 && (WIN_ != 0 || PG_ == 64);
+    static constexpr bool VDMA = !VT && KV != KV_MXFP4 && (NT_ == 1 || NT2_DMA) && !(KV_ == KV_BF16 && PG_ == 128);
     static constexpr bool STAGE_V = !VT && !VDMA;
     // Whole-stage prefetch (fp8 caches with per-token scales on the LDS-DMA
     // path, one workgroup per CU): the K, V and scale loads of a wave's next
@@ -213,16 +227,19 @@ struct Cfg {
     // for everything outstanding before using a register loaded ahead of an
     // LDS DMA, so register loads cannot be kept in flight across a DMA wait;
     // hence the one full wait at the top.)
-    static constexpr bool PF = VDMA && KV_ == KV_FP8 && SC_ == SC_TOKEN;
+    static constexpr bool PF = VDMA && KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 1;
+    // query fragments in LDS (one copy per workgroup) instead of registers
+    static constexpr bool QLDS = NT2_DMA;
     static constexpr int VPITCH = D * 2 + 16;                        // staged bf16 row pitch in bytes
     static constexpr int CPR = ROWB / 16;                            // 16-byte chunks per V row (DMA)
     static constexpr int VSTAGE_BYTES = VDMA ? 64 * ROWB : (STAGE_V ? 32 * VPITCH : 0);  // per wave
     static constexpr int SCALE_BYTES = PF ? 512 : 0;                 // K then V scales of 64 tokens (fp32)
     static constexpr int WAVE_LDS = (PF ? 2 : 1) * (VSTAGE_BYTES + SCALE_BYTES);  // per wave
+    static constexpr int QLDS_BYTES = QLDS ? NT * KSTEPS * 64 * 16 : 0;
     static constexpr int ROWS_PAD = 16 * NT;
     static constexpr int OPITCH = D + 4;                             // floats
     static constexpr int EPI_BYTES = 2 * ROWS_PAD * OPITCH * 4 + 2 * 4 * ROWS_PAD * 4;
-    static constexpr int SMEM = (4 * WAVE_LDS > EPI_BYTES) ? 4 * WAVE_LDS : EPI_BYTES;
+    static constexpr int SMEM = (4 * WAVE_LDS + QLDS_BYTES > EPI_BYTES) ? 4 * WAVE_LDS + QLDS_BYTES : EPI_BYTES;
     // staging geometry for token-major V loads
     static constexpr int LPR = ROWB / 16;         // lanes per token row
     static constexpr int TPI = 64 / LPR;          // tokens per load instruction
@@ -618,9 +635,12 @@ PA_DEV void load_v(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, VB
 }
 
 // QK, scale, mask, online softmax (base 2) -> P^T fragments.
+// qlds (QLDS instances): the query fragments in LDS, fragment (nt, ks) of lane
+// l at byte 16 ((nt KSTEPS + ks) 64 + l); restrict-qualified, as the slice's V
+// DMA is in flight while they are read.
 template <class C, bool MASK>
 PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, const KBuf<C>& kb, State<C>& st,
-                       PFrag<C>& pf, int cb) {
+                       PFrag<C>& pf, int cb, const char* __restrict__ qlds = nullptr) {
     constexpr int NT = C::NT;
     const int lg = cx.lg;
     // S^T[token][row]; acc[c][nt][j] <-> slice token 16*lg + 4c + j, row 16nt + ln
@@ -630,7 +650,16 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (C::MXS) {
+            if constexpr (C::QLDS) {
+#pragma unroll
+                for (int u = 0; u < C::KLOADS; ++u) {
+                    const u32x4 q0 = *reinterpret_cast<const u32x4*>(qlds + 16 * ((nt * C::KSTEPS + 2 * u) * 64 + cx.lane));
+                    const u32x4 q1 =
+                        *reinterpret_cast<const u32x4*>(qlds + 16 * ((nt * C::KSTEPS + 2 * u + 1) * 64 + cx.lane));
+                    s = mfma_bf16(fp8x8_to_bf16x8(kb.k[c][u][0], kb.k[c][u][1]), as_bf16x8(q0), s);
+                    s = mfma_bf16(fp8x8_to_bf16x8(kb.k[c][u][2], kb.k[c][u][3]), as_bf16x8(q1), s);
+                }
+            } else if constexpr (C::MXS) {
                 i32x8 ka = {(int)kb.k[c][0][0], (int)kb.k[c][0][1], (int)kb.k[c][0][2], (int)kb.k[c][0][3], 0, 0, 0, 0};
                 s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qf.q8[nt], s, 4, 0, 0,
                                                                      (int)((kb.ksc[c] >> (8 * lg)) & 0xFFu), 0,
@@ -652,6 +681,9 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
                 }
             }
             acc[c][nt] = s;
+            // QLDS: keep one 16-token group's K conversions and query reads
+            // from being hoisted above the previous group's products
+            if constexpr (C::QLDS) __builtin_amdgcn_sched_barrier(0);
         }
 
     const float sc = a.scale_log2 * cx.kscale;
@@ -959,6 +991,19 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     }
 
     char* vlds = smem + cx.wave * C::WAVE_LDS;
+    char* qlds = smem + 4 * C::WAVE_LDS;
+    if constexpr (C::QLDS) {
+        // one copy of the query fragments for the workgroup (the same for every wave)
+        if (cx.wave == 0) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int ks = 0; ks < C::KSTEPS; ++ks)
+                    *reinterpret_cast<u32x4*>(qlds + 16 * ((nt * C::KSTEPS + ks) * 64 + cx.lane)) =
+                        __builtin_bit_cast(u32x4, qf.q[nt][ks]);
+        }
+        __syncthreads();
+    }
 
     // Query row r of this lane (query token i = r / G) attends to
     // [row_s, row_e): e = L - qlen + i + 1 when causal, else L; s = e - window
@@ -1059,7 +1104,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
             dma_fence<C>();
             load_v<C>(a, cx, sp, vb, vlds);
             PFrag<C> pf;
-            qk_softmax<C, M>(a, cx, qf, kb, st, pf, cb);
+            qk_softmax<C, M>(a, cx, qf, kb, st, pf, cb, qlds);
             sp = slice_pages<C>(a, cx, pc, tile + 1);
             load_k<C>(a, cx, sp, kb);
             pv<C, M, C::KVMEM>(cx, vb, pf, st, cb, vlds);
@@ -1076,7 +1121,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
         dma_fence<C>();
         load_v<C>(a, cx, sp, vb, vlds);
         PFrag<C> pf;
-        qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb);
+        qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb, qlds);
         pv<C, true, 0>(cx, vb, pf, st, cb, vlds);
     }
 

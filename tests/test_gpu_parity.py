@@ -245,6 +245,11 @@ GPU_MASK_SPECS = [
            window=600),
     I.Spec("g_fp8tok_d256_p128_q2_causal", 3, ("fixed", (1, 383, 1800)), 2, 1, 8, 256, 128, "fp8", "token",
            seed=49, causal=1),
+    # fp8 per-token caches with 32 query rows at head_dim 256 on the V-by-DMA
+    # path (query fragments in LDS): page 64 plain, page 128 causal + window
+    I.Spec("g_fp8tok_d256_p64_q4", 3, ("fixed", (2, 900, 2100)), 4, 1, 8, 256, 64, "fp8", "token", seed=50),
+    I.Spec("g_fp8tok_d256_p128_q4_causal_win", 3, ("fixed", (3, 700, 2000)), 4, 1, 8, 256, 128, "fp8", "token",
+           seed=51, causal=1, window=600),
 ]
 
 
