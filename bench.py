@@ -126,7 +126,7 @@ def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
     kernels = {}
     lines = ["| workload | tile kernel | dispatches | HBM read B/launch | HBM write B/launch | algorithmic B | read / algorithmic |",
              "|---|---|---|---|---|---|---|"]
-    for spec in (I.BF16_P64, I.BF16_P128, I.FP8TOK_Q1, I.FP8TOK_Q4):
+    for spec in (I.BF16_P64, I.BF16_P128, I.FP8TOK_Q1, I.FP8TOK_Q4, I.FP8TOK_Q4_CAUSAL):
         tag = kernel_tag_of(spec)
         if spec.kv_dtype != "bf16" and not any(tag in k for k in fetch):
             continue  # the fp8 rows only when the run included them (--all --workloads ...)
@@ -227,7 +227,8 @@ def time_all(steps, warmup, names=None):
     Each event pair also brackets the event packets' own queue time (a few us,
     which is a tenth of a 60 us call). So a second, differential figure is taken
     too: `steps` cold calls (flush, call, flush, call, ...) between two events,
-    minus `steps` flushes alone between two events, divided by `steps`."""
+    minus `steps` flushes alone between two events, divided by `steps` (median
+    of five alternating pairs of batches)."""
     import statistics
 
     import torch
@@ -260,21 +261,26 @@ def time_all(steps, warmup, names=None):
             b.record()
         torch.cuda.synchronize()
         us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
-        # differential cold time: the event packets' cost is paid once per batch
+        # differential cold time: the event packets' cost is paid once per batch;
+        # batches with and without the calls alternate, and the median of five
+        # differences is kept (the flushes alone vary by about 1 % between batches)
         a, b = ev[0]
-        a.record()
-        for _ in range(steps):
-            torch.amax(flush, dim=0, out=flush_out)
-            call()
-        b.record()
-        torch.cuda.synchronize()
-        t_calls = a.elapsed_time(b)
-        a.record()
-        for _ in range(steps):
-            torch.amax(flush, dim=0, out=flush_out)
-        b.record()
-        torch.cuda.synchronize()
-        us_diff = (t_calls - a.elapsed_time(b)) * 1e3 / steps
+        diffs = []
+        for _ in range(5):
+            a.record()
+            for _ in range(steps):
+                torch.amax(flush, dim=0, out=flush_out)
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            t_calls = a.elapsed_time(b)
+            a.record()
+            for _ in range(steps):
+                torch.amax(flush, dim=0, out=flush_out)
+            b.record()
+            torch.cuda.synchronize()
+            diffs.append((t_calls - a.elapsed_time(b)) * 1e3 / steps)
+        us_diff = statistics.median(diffs)
         prob = pa.problem_of(case)
 
         def call_direct():
