@@ -248,6 +248,9 @@ GPU_MASK_SPECS = [
     # fp8 per-token caches with 32 query rows at head_dim 256 on the V-by-DMA
     # path (query fragments in LDS): page 64 plain, page 128 causal + window
     I.Spec("g_fp8tok_d256_p64_q4", 3, ("fixed", (2, 900, 2100)), 4, 1, 8, 256, 64, "fp8", "token", seed=50),
+    # whole-stage prefetch, no mask rows: page 64 qlen 1, page 128 qlen 2 (16 rows)
+    I.Spec("g_fp8tok_d256_p64_q1", 3, ("fixed", (63, 1025, 2300)), 1, 2, 8, 256, 64, "fp8", "token", seed=52),
+    I.Spec("g_fp8tok_d256_p128_q2", 3, ("fixed", (128, 257, 1900)), 2, 1, 8, 256, 128, "fp8", "token", seed=53),
     I.Spec("g_fp8tok_d256_p128_q4_causal_win", 3, ("fixed", (3, 700, 2000)), 4, 1, 8, 256, 128, "fp8", "token",
            seed=51, causal=1, window=600),
 ]
