@@ -216,6 +216,11 @@ struct Cfg {
     static constexpr bool NT2_DMA = KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 2 && D_ == 256 && (WIN_ != 0 || PG_ == 64);
     static constexpr bool VDMA = !VT && KV != KV_MXFP4 && (NT_ == 1 || NT2_DMA) && !(KV_ == KV_BF16 && PG_ == 128);
     static constexpr bool STAGE_V = !VT && !VDMA;
+    // Register-staged V loads held at the top of the slice (see load_v): for
+    // the fp8 per-token page-16 instance with 32 query rows at head_dim 256,
+    // where it also removes every spill (qlen 4, batch 16: 80.7 -> 76.2 us per
+    // call); at page 128 it adds a spill reload to the loop (80.1 -> 86.9 us).
+    static constexpr bool PIN_V = STAGE_V && KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 2 && D_ == 256 && PG_ == 16;
     // Whole-stage prefetch (fp8 caches with per-token scales on the LDS-DMA
     // path, one workgroup per CU): the K, V and scale loads of a wave's next
     // slice are all issued at the top of the current one, into a second K
@@ -621,6 +626,10 @@ PA_DEV void load_v(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, VB
                 vb.v[s][i] = ld16_kv(cx.vbase + row * C::ROWB + 16 * vseg);
                 if constexpr (C::KV == KV_MXFP4) vb.vsc[s][i] = ld4_kv(cx.vsbase + row * C::SROWB);  // byte vseg is used
             }
+        // keep these loads at the top of the slice, ahead of QK: left alone, the
+        // scheduler sinks them below QK, right before the staging that waits
+        // for them, and the slice then pays the whole V latency
+        if constexpr (C::PIN_V) __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (C::VT) {
         // lane (d = 16dt + ln, lg) holds slice tokens 16*lg + [0, 16) of row d
