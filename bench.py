@@ -126,10 +126,11 @@ def write_traffic(fetch_csv: str, write_csv: str, out_json: str):
     kernels = {}
     lines = ["| workload | tile kernel | dispatches | HBM read B/launch | HBM write B/launch | algorithmic B | read / algorithmic |",
              "|---|---|---|---|---|---|---|"]
-    for spec in (I.BF16_P64, I.BF16_P128, I.FP8TOK_Q1, I.FP8TOK_Q4, I.FP8TOK_Q4_CAUSAL):
+    for spec in (I.BF16_P64, I.BF16_P128, I.FP8TOK_Q1, I.FP8TOK_Q4, I.FP8TOK_Q4_CAUSAL, I.FP8_TRANS, I.MXFP4_LONG_Q8,
+                 I.MXFP4_LONG_QBF):
         tag = kernel_tag_of(spec)
         if spec.kv_dtype != "bf16" and not any(tag in k for k in fetch):
-            continue  # the fp8 rows only when the run included them (--all --workloads ...)
+            continue  # rows other than bf16 only when the run included them (--all --workloads ...)
         fv, wv = one(fetch, tag), one(write, tag)
         rd = sum(fv) / len(fv) * 1024 * f_factor
         wr = sum(wv) / len(wv) * 1024 * w_factor
