@@ -75,7 +75,8 @@ def kernel_tag_of(spec) -> str:
     kv = {"bf16": 0, "fp8": 1, "mxfp4": 2}[spec.kv_dtype]
     sc = {"none": 0, "tensor": 1, "token": 2}[spec.scale_mode]
     vt = 1 if spec.v_layout == "trans" else 0
-    nt = 1 if spec.qlen * spec.q_per_kv <= 16 else 2
+    rows = spec.qlen * spec.q_per_kv
+    nt = 1 if rows <= 16 else (2 if rows <= 32 else 4)
     qf = 1 if spec.q_dtype == "fp8" else 0
     win = 1 if spec.window > 0 or (spec.causal and spec.qlen > 1) else 0
     return "Cfg<%d, %d, %d, %d, %d, %d, %d, 0, %d>" % (kv, sc, vt, spec.head_dim, spec.page_size, nt, qf, win)

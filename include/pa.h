@@ -15,9 +15,10 @@
  *   L = 0     -> out row = 0
  *
  * Rows no sequence owns (block 0 pinned pages, the tail of a sequence's last
- * page, anything at or past L) never influence out: their scores are -inf,
- * and on the boundary tile their V bytes and per-token scales are zeroed
- * before the P*V product (PR #7092, section "Fix"). NaN/Inf there is harmless.
+ * page, anything at or past L, and with a sliding window anything before every
+ * query row's window) never influence out: their scores are -inf, and on the
+ * masked tiles their V bytes and per-token scales are zeroed before the P*V
+ * product (PR #7092, section "Fix"). NaN/Inf there is harmless.
  *
  * Everything is plain C: pointers, sizes and enums. PyTorch (or any caller)
  * owns the device tensors; the library owns only what pa_plan allocates.
@@ -75,7 +76,12 @@ typedef enum pa_q_dtype { PA_Q_BF16 = 0, PA_Q_FP8_E4M3 = 1 } pa_q_dtype;
 
 /* Problem descriptor. All sizes are element counts unless stated.
  *   num_seqs            B, sequences in the batch (>= 0)
- *   qlen                query tokens per sequence (1..4 typical; rows = qlen * q_per_kv <= 32)
+ *   qlen                query tokens per sequence (1..4 typical). rows = qlen * q_per_kv
+ *                       query rows share a KV head: at most 64, and at most 32
+ *                       with head_dim 256 (64 rows at head_dim 256 would need 256
+ *                       accumulator registers per lane for O alone); ROCm/aiter
+ *                       PR #7092, "Tests": its unowned-row matrix has a 64-row
+ *                       case (qlen 4, GQA 16, head_dim 128)
  *   num_kv_heads        Hkv
  *   q_per_kv            G, query heads per KV head (Hq = Hkv * G)
  *   head_dim            D: 128 or 256 (MXFP4: 128)
@@ -104,10 +110,20 @@ typedef enum pa_q_dtype { PA_Q_BF16 = 0, PA_Q_FP8_E4M3 = 1 } pa_q_dtype;
  *                       probes; the causal select of the later tile commit).
  *   window              0 (default): no sliding window. W > 0: token i attends
  *                       only to t >= e_i - W as well (the W positions ending at
- *                       its own). Tiles and block-table columns wholly before
- *                       every row's window are never read. A row whose range is
- *                       empty is written as 0. Not offered with MXFP4 ([P2]
- *                       "Summary": sliding window is refused there).
+ *                       its own). Let s_lo = max(0, e_0 - W), the start of the
+ *                       earliest row's window (e_0 = L - qlen + 1 when causal,
+ *                       else L). Tokens before s_lo are seen by no row and are
+ *                       treated like tokens at or past L: block-table columns
+ *                       j < floor(s_lo / page_size) (pages wholly before s_lo)
+ *                       are never read, and tokens of the page holding s_lo
+ *                       that lie before it may hold anything (NaN, Inf,
+ *                       garbage, including their per-token scales): their
+ *                       scores are -inf and their V bytes and V scales are
+ *                       zeroed before P*V. Tokens in [s_lo, L) must hold the
+ *                       sequence's data even where some rows do not see them.
+ *                       A row whose range is empty is written as 0. Not offered
+ *                       with MXFP4 ([P2] "Summary": sliding window is refused
+ *                       there).
  */
 typedef struct pa_problem {
     int32_t num_seqs;
@@ -147,8 +163,10 @@ typedef void* pa_stream_t;
  *
  * host_context_lens: optional host int32[num_seqs]. With it, partitions follow
  * the real lengths (the device lengths passed to pa_decode must then be equal
- * or shorter). Without it, every sequence is split as if it had
- * max_context_len tokens and the kernels clamp to the device lengths.
+ * or shorter; with a window, a sequence's first partition starts at the device
+ * window's first tile, so a shorter device length still covers its window).
+ * Without it, every sequence is split as if it had max_context_len tokens and
+ * the kernels clamp to the device lengths.
  *
  * Ownership: *plan_out belongs to the caller; release it with pa_plan_destroy.
  * Refusals: see pa_status. A host length above max_blocks_per_seq * page_size
@@ -174,7 +192,9 @@ pa_status pa_plan(const pa_problem* problem, const int32_t* host_context_lens, p
  *   out           bf16 [B][qlen][Hq][D]; every element is written
  *
  * Device-side guarantees: block_tables columns >= ceil(L/page) are never read;
- * tiles past ceil(L/256) are never read; tokens >= L never affect out; page ids
+ * tiles past ceil(L/256) are never read; tokens >= L never affect out; with a
+ * window, columns and tokens before s_lo (see pa_problem.window) are treated
+ * the same way; page ids
  * outside [0, num_blocks) and lengths outside [0, max_blocks_per_seq * page]
  * are clamped so that no access leaves the caller's buffers (the output of
  * such a sequence is then unspecified).

@@ -100,8 +100,15 @@ pa_status validate(const pa_problem* p) {
         return fail(PA_ERR_UNSUPPORTED, "page_size %d (supported: 16, 64, 128)", p->page_size);
     if (p->head_dim != 128 && p->head_dim != 256)
         return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 128, 256)", p->head_dim);
-    if (rows_of(*p) > 32)
-        return fail(PA_ERR_UNSUPPORTED, "qlen * q_per_kv = %d query rows per KV head (supported: <= 32)", rows_of(*p));
+    if (rows_of(*p) > 64)
+        return fail(PA_ERR_UNSUPPORTED, "qlen * q_per_kv = %d query rows per KV head (supported: <= 64)", rows_of(*p));
+    // 33-64 rows take four 16-row N tiles, whose fp32 accumulators alone need
+    // head_dim / 16 * 4 * 4 registers per lane: 128 at head_dim 128, 256 at 256,
+    // which leaves no room for K, the scores and the softmax state
+    if (rows_of(*p) > 32 && p->head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED,
+                    "qlen * q_per_kv = %d query rows per KV head with head_dim %d (more than 32 rows: head_dim 128 only)",
+                    rows_of(*p), p->head_dim);
     if ((long long)p->max_blocks_per_seq * p->page_size > (1LL << 30))
         return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^30 tokens");
     if (p->kv_dtype == PA_KV_BF16) {
@@ -133,7 +140,7 @@ pa::KernelKey key_of(const pa_problem& p) {
     k.vt = p.v_layout == PA_V_TRANSPOSED ? 1 : 0;
     k.head_dim = p.head_dim;
     k.page = p.page_size;
-    k.ntiles_n = rows_of(p) <= 16 ? 1 : 2;
+    k.ntiles_n = rows_of(p) <= 16 ? 1 : (rows_of(p) <= 32 ? 2 : 4);
     k.q_fp8 = p.q_dtype == PA_Q_FP8_E4M3 ? 1 : 0;
     k.mx_scaled = (p.kv_dtype == PA_KV_MXFP4 && p.mxfp4_scaled_qk) ? 1 : 0;
     k.win = (p.window > 0 || (p.causal && p.qlen > 1)) ? 1 : 0;  // qlen 1: causal is the plain decode

@@ -181,8 +181,16 @@ struct Cfg {
     // P enters PV as bf16 hi + lo parts (two MFMAs) for MXFP4: its softmax is
     // near one-hot and its V rows reach 6 * 2^9, so bf16 rounding of a
     // runner-up weight alone would move an output element by far more than the
-    // element bound wherever the mixed V rows cancel
-    static constexpr bool PSPLIT = KV == KV_MXFP4;
+    // element bound wherever the mixed V rows cancel. Also with per-token V
+    // scales: the weight P * v_scale has no exact bf16 form and the weight
+    // sum cannot share its rounding, so one bf16 rounding adds about 2^-9 / 3
+    // of relative error per weight on top of the bf16 output rounding (rel-L2
+    // 2.95e-3 against a 2.30e-3 output-rounding floor on 64 rows of a mixed
+    // short-length batch); hi + lo leaves only the output rounding. Not at
+    // head_dim 256 with 32 query rows, where the low parts' registers make the
+    // register-staged loop spill; one rounding there gives rel-L2 2.4e-3 on
+    // the qlen-4 batch against a 1.7e-3 floor.
+    static constexpr bool PSPLIT = KV == KV_MXFP4 || (SC_ == SC_TOKEN && !(NT_ == 2 && D_ == 256));
     static constexpr int ESZ = KV == KV_BF16 ? 2 : 1;                // bytes per bf16/fp8 element
     static constexpr int ROWB = KV == KV_MXFP4 ? D / 2 : D * ESZ;    // bytes of one token row (data)
     static constexpr int SROWB = KV == KV_MXFP4 ? D / 32 : 0;        // bytes of one token's e8m0 scales
@@ -214,7 +222,12 @@ struct Cfg {
     // The plain page-16 and page-128 instances keep register staging, whose
     // loops do not spill and which measured faster there (80-81 against 99 us).
     static constexpr bool NT2_DMA = KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 2 && D_ == 256 && (WIN_ != 0 || PG_ == 64);
-    static constexpr bool VDMA = !VT && KV != KV_MXFP4 && (NT_ == 1 || NT2_DMA) && !(KV_ == KV_BF16 && PG_ == 128);
+    // 64 query rows (four N tiles, head_dim 128 only): the accumulators alone
+    // take 128 registers, so V always goes by LDS DMA and the query fragments
+    // live in LDS, leaving the registers to K, the scores and O.
+    static constexpr bool NT4 = NT_ == 4;
+    static constexpr bool VDMA = !VT && KV != KV_MXFP4 && (NT_ == 1 || NT2_DMA || NT4) &&
+                                 !(KV_ == KV_BF16 && PG_ == 128 && !NT4);
     static constexpr bool STAGE_V = !VT && !VDMA;
     // Register-staged V loads held at the top of the slice (see load_v): for
     // the fp8 per-token page-16 instance with 32 query rows at head_dim 256,
@@ -234,7 +247,7 @@ struct Cfg {
     // hence the one full wait at the top.)
     static constexpr bool PF = VDMA && KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 1;
     // query fragments in LDS (one copy per workgroup) instead of registers
-    static constexpr bool QLDS = NT2_DMA;
+    static constexpr bool QLDS = NT2_DMA || NT4;
     static constexpr int VPITCH = D * 2 + 16;                        // staged bf16 row pitch in bytes
     static constexpr int CPR = ROWB / 16;                            // 16-byte chunks per V row (DMA)
     static constexpr int VSTAGE_BYTES = VDMA ? 64 * ROWB : (STAGE_V ? 32 * VPITCH : 0);  // per wave
@@ -285,7 +298,13 @@ struct State {
 
 struct Ctx {
     int b, kvh, L, npages, lane, ln, lg, wave;
-    int row_s[2], row_e[2];  // token range [row_s, row_e) of this lane's query row in N tile 0 / 1
+    // With causal rows or a window: s_lo is the smallest row start of the
+    // call. Tokens before it are seen by no row and are treated like tokens
+    // at or past L (V bytes and per-token V scales zeroed on masked tiles);
+    // table columns before pg_first (= s_lo / page) lie wholly before it and
+    // are never read. Without a mask both are 0.
+    int s_lo, pg_first;
+    int row_s[4], row_e[4];  // token range [row_s, row_e) of this lane's query row in N tile nt
     const int32_t* bt_row;
     const char* kbase;   // K data of this head in page 0
     const char* vbase;   // V data of this head in page 0
@@ -399,15 +418,15 @@ PA_DEV void load_q(const TileArgs& a, const Ctx& cx, QFrag<C>& qf) {
 }
 
 // Page id of table slot `slot` (pinned to block 0 past the owned pages and
-// clamped into the pool).
+// before the first column any row reads, and clamped into the pool).
 template <bool MASK>
 PA_DEV int page_of(const TileArgs& a, const Ctx& cx, int slot) {
     // The read is unconditional, since a per-lane branch here would make every
-    // loop that refills page ids divergent. Past the owned pages it re-reads
-    // the last owned column, and the select pins the slot to block 0.
-    const int col = MASK ? min(slot, max(cx.npages - 1, 0)) : slot;
+    // loop that refills page ids divergent. Outside the read columns it
+    // re-reads the nearest one, and the select pins the slot to block 0.
+    const int col = MASK ? min(max(slot, cx.pg_first), max(cx.npages - 1, 0)) : slot;
     int p = cx.bt_row[col];
-    if (MASK && slot >= cx.npages) p = 0;
+    if (MASK && (slot >= cx.npages || slot < cx.pg_first)) p = 0;
     p = p < 0 ? 0 : (p >= a.num_blocks ? a.num_blocks - 1 : p);
     return p;
 }
@@ -659,7 +678,13 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (C::QLDS) {
+            if constexpr (C::QLDS && C::KV == KV_BF16) {
+#pragma unroll
+                for (int ks = 0; ks < C::KSTEPS; ++ks) {
+                    const u32x4 q = *reinterpret_cast<const u32x4*>(qlds + 16 * ((nt * C::KSTEPS + ks) * 64 + cx.lane));
+                    s = mfma_bf16(as_bf16x8(kb.k[c][ks]), as_bf16x8(q), s);
+                }
+            } else if constexpr (C::QLDS) {
 #pragma unroll
                 for (int u = 0; u < C::KLOADS; ++u) {
                     const u32x4 q0 = *reinterpret_cast<const u32x4*>(qlds + 16 * ((nt * C::KSTEPS + 2 * u) * 64 + cx.lane));
@@ -700,8 +725,10 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
     if constexpr (C::SC == SC_TOKEN) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            // per-token V scales of tokens at or past L are staged as 0 (PR #7092, "Fix")
-            tvs[i] = (!MASK || cb + 16 * lg + i < cx.L) ? kb.tvs[i] : 0.f;
+            // per-token V scales of tokens at or past L, or before every row's
+            // window, are staged as 0 (PR #7092, "Fix")
+            const int tok = cb + 16 * lg + i;
+            tvs[i] = (!MASK || (tok < cx.L && (!C::WIN || tok >= cx.s_lo))) ? kb.tvs[i] : 0.f;
         }
     }
 #pragma unroll
@@ -733,17 +760,21 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
             float p[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) p[j] = fast_exp2(acc[c][nt][j] - muse);
-            uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);
+            // the weight sum: of P in fp32 where PV's weights are not the bf16
+            // P itself (hi + lo parts, or P times a per-token V scale)
+            if constexpr (C::PSPLIT || C::SC == SC_TOKEN) lsum += (p[0] + p[1]) + (p[2] + p[3]);
+            // the PV weight: P times the token's V scale in fp32, rounded once
+            if constexpr (C::SC == SC_TOKEN) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[j] *= tvs[4 * c + j];
+            }
+            const uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);
             if constexpr (C::PSPLIT) {
                 plo[2 * c] = pack_bf16(p[0] - bf16_lo(w0), p[1] - bf16_hi(w0));
                 plo[2 * c + 1] = pack_bf16(p[2] - bf16_lo(w1), p[3] - bf16_hi(w1));
-                lsum += (p[0] + p[1]) + (p[2] + p[3]);
-            } else {
+            } else if constexpr (C::SC != SC_TOKEN) {
+                // the weight sum of exactly the rounded weights PV uses
                 lsum += (bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1));
-            }
-            if constexpr (C::SC == SC_TOKEN) {
-                w0 = pack_bf16(bf16_lo(w0) * tvs[4 * c + 0], bf16_hi(w0) * tvs[4 * c + 1]);
-                w1 = pack_bf16(bf16_lo(w1) * tvs[4 * c + 2], bf16_hi(w1) * tvs[4 * c + 3]);
             }
             pw[2 * c] = w0;
             pw[2 * c + 1] = w1;
@@ -788,14 +819,16 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
 #pragma unroll
             for (int w = 0; w < VTW; ++w) vt[dt][w] = vb.vt[dt][w];
         if (MASK) {
-            // keep only the bytes of tokens < L (byte-granular, PR #7092 "Fix")
+            // keep only the bytes of tokens in [s_lo, L) (byte-granular, PR #7092 "Fix")
             const int valid = cx.L - (cb + 16 * lg);  // owned tokens among this lane's 16
+            const int lead = C::WIN ? cx.s_lo - (cb + 16 * lg) : 0;  // of them, before every window
 #pragma unroll
             for (int w = 0; w < VTW; ++w)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int first = (16 * w + 4 * j) / C::ESZ;  // first token of this dword
-                    const uint32_t mk = keep_bytes((valid - first) * C::ESZ);
+                    uint32_t mk = keep_bytes((valid - first) * C::ESZ);
+                    if constexpr (C::WIN) mk &= ~keep_bytes((lead - first) * C::ESZ);
 #pragma unroll
                     for (int dt = 0; dt < C::DT; ++dt) vt[dt][w][j] &= mk;
                 }
@@ -816,7 +849,7 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
             for (int i = 0; i < C::IPS; ++i) {
                 const int e = i * C::TPI + lane / C::LPR;
                 const int t = 16 * (e >> 3) + 8 * s + (e & 7);
-                const bool ok = !MASK || (cb + t < cx.L);
+                const bool ok = !MASK || (cb + t < cx.L && (!C::WIN || cb + t >= cx.s_lo));
                 char* dst = vlds + e * C::VPITCH;
                 u32x4 raw = vb.v[s][i];
                 if constexpr (C::KV == KV_BF16) {
@@ -879,27 +912,33 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
                 for (int k = 0; k < CH; ++k) {
                     const int dt = d0 + k;
                     // element / byte e of this lane is token cb + 16g + 8s + e: zero
-                    // those at or past L (PR #7092, "Fix")
+                    // those at or past L, and those before every row's window
+                    // (PR #7092, "Fix")
                     const int valid = cx.L - (cb + 16 * lg + 8 * s);
+                    const int lead = C::WIN ? cx.s_lo - (cb + 16 * lg + 8 * s) : 0;
                     bf16x8 va;
                     if constexpr (C::KV == KV_BF16) {
                         u32x4 w = raw[k];
                         if (MASK) {
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                w[j] &= (valid > 2 * j ? 0x0000FFFFu : 0u) | (valid > 2 * j + 1 ? 0xFFFF0000u : 0u);
+                                w[j] &= (valid > 2 * j && lead <= 2 * j ? 0x0000FFFFu : 0u) |
+                                        (valid > 2 * j + 1 && lead <= 2 * j + 1 ? 0xFFFF0000u : 0u);
                         }
                         va = as_bf16x8(w);
                     } else {
                         uint32_t b0 = raw[k][0], b1 = raw[k][1];
                         if (MASK) {
-                            b0 &= keep_bytes(valid);
-                            b1 &= keep_bytes(valid - 4);
+                            b0 &= keep_bytes(valid) & ~keep_bytes(lead);
+                            b1 &= keep_bytes(valid - 4) & ~keep_bytes(lead - 4);
                         }
                         va = fp8x8_to_bf16x8(b0, b1);
                     }
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pf.hi[s][nt]), st.o[dt][nt]);
+                    for (int nt = 0; nt < NT; ++nt) {
+                        st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pf.hi[s][nt]), st.o[dt][nt]);
+                        if constexpr (C::PSPLIT) st.o[dt][nt] = mfma_bf16(va, as_bf16x8(pf.lo[s][nt]), st.o[dt][nt]);
+                    }
                 }
             }
             continue;
@@ -1018,7 +1057,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     // [row_s, row_e): e = L - qlen + i + 1 when causal, else L; s = e - window
     // with a sliding window, else 0.
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         if constexpr (C::WIN) {
             const int r = 16 * nt + cx.ln;
             const int i = r < a.rows ? r / a.q_per_kv : a.qlen - 1;
@@ -1031,7 +1070,11 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
         }
     }
     // Tiles of the task: [T0, T1), the task's range cut to the tiles any row
-    // reads (from the first row's window start to ceil(L / 256)). Tiles
+    // reads (from the first row's window start to ceil(L / 256)). The first
+    // partition of a sequence starts at the device window's first tile
+    // whatever the plan says: a plan made from host lengths cuts the tiles
+    // before the host window, and a shorter device length moves the window
+    // earlier (the other partitions' ranges then still cover the rest). Tiles
     // [F0, F1) lie inside every row's range and run unmasked; the others
     // (the window's first tiles, the causal and context boundary at the end)
     // run the masked variant. Loads run one stage ahead: V(j) is issued at
@@ -1043,7 +1086,9 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     const int e_min = C::WIN ? max(0, a.causal ? L - a.qlen + 1 : L) : L;  // smallest row end
     const int s_min = C::WIN && a.window > 0 ? max(0, e_min - a.window) : 0;
     const int s_max = C::WIN && a.window > 0 ? max(0, L - a.window) : 0;
-    const int T0 = max(tb, s_min / kTileTokens);
+    const int T0 = part == 0 ? s_min / kTileTokens : max(tb, s_min / kTileTokens);
+    cx.s_lo = s_min;
+    cx.pg_first = C::WIN ? min(s_min / PG, max(cx.npages - 1, 0)) : 0;
     const int T1 = te;
     const int F0 = max(T0, (s_max + kTileTokens - 1) / kTileTokens);
     const int F1 = max(F0, min(T1, e_min / kTileTokens));
@@ -1333,7 +1378,7 @@ struct Entry {
 #define PA_PG(KV, SC, VT, D, NT, W) \
     PA_E(KV, SC, VT, D, 16, NT, 0, W), PA_E(KV, SC, VT, D, 64, NT, 0, W), PA_E(KV, SC, VT, D, 128, NT, 0, W)
 #define PA_NT(KV, SC, VT, D, W) PA_PG(KV, SC, VT, D, 1, W), PA_PG(KV, SC, VT, D, 2, W)
-#define PA_D(KV, SC, VT, W) PA_NT(KV, SC, VT, 128, W), PA_NT(KV, SC, VT, 256, W)
+#define PA_D(KV, SC, VT, W) PA_NT(KV, SC, VT, 128, W), PA_PG(KV, SC, VT, 128, 4, W), PA_NT(KV, SC, VT, 256, W)
 #define PA_VT(KV, SC, W) PA_D(KV, SC, 0, W), PA_D(KV, SC, 1, W)
 
 #if PA_IN_SHARD(0)

@@ -645,3 +645,52 @@ def owned_mask(case: Case) -> torch.Tensor:
             p = int(case.block_tables[b, j])
             m[p, :min(PG, L - j * PG)] = True
     return m
+
+
+def window_start(case: Case, b: int) -> int:
+    """s_lo of sequence b: the first token any query row's window covers (0
+    without a window). Row i's window ends at e_i = L - qlen + i + 1 when
+    causal, else L, and starts W tokens earlier; row 0 starts first."""
+    if not getattr(case, "window", 0):
+        return 0
+    L = int(case.context_lens[b])
+    e0 = L - case.qlen + 1 if case.causal else L
+    return max(0, e0 - case.window)
+
+
+def poison_prewindow(case: Case, fill: str, seed: Optional[int] = None) -> Case:
+    """A copy of `case` (unowned rows refilled with `fill`) in which everything
+    before each sequence's window start s_lo is treated as freed: table
+    columns wholly before s_lo point at block 0, and the rows of the page
+    holding s_lo that lie before it -- K, V and per-token scales -- hold
+    `fill` too. A caller that releases the pages a sliding window has left
+    behind leaves exactly this state."""
+    seed = case.spec.seed if seed is None else seed
+    base = refill(case, fill, seed)
+    gp = torch.Generator().manual_seed(seed + 104729)
+    K, V = base.key_cache.clone(), base.value_cache.clone()
+    token_scales = case.kv_dtype == "fp8" and case.scale_mode == "token"
+    ks = base.k_scale.clone() if token_scales else base.k_scale
+    vs = base.v_scale.clone() if token_scales else base.v_scale
+    bt = base.block_tables.clone()
+    PG, H, D = case.page_size, case.num_kv_heads, case.head_dim
+    kind = "bf16" if case.kv_dtype == "bf16" else "u8"
+    trans = case.v_layout == "trans"
+    for b in range(case.num_seqs):
+        s = window_start(case, b)
+        c, n = s // PG, s % PG
+        bt[b, :c] = 0
+        if n == 0:
+            continue
+        p = int(case.block_tables[b, c])
+        Ks = K.view(torch.int16) if kind == "bf16" else K
+        Vs = V.view(torch.int16) if kind == "bf16" else V
+        Ks[p, :, :n, :] = _poison_value(kind, fill, gp, H * n * D).view(H, n, D)
+        if trans:
+            Vs[p, :, :, :n] = _poison_value(kind, fill, gp, H * D * n).view(H, D, n)
+        else:
+            Vs[p, :, :n, :] = _poison_value(kind, fill, gp, H * n * D).view(H, n, D)
+        if token_scales:
+            ks[p, :, :n] = _poison_value("f32", fill, gp, H * n).view(H, n)
+            vs[p, :, :n] = _poison_value("f32", fill, gp, H * n).view(H, n)
+    return dataclasses.replace(base, key_cache=K, value_cache=V, k_scale=ks, v_scale=vs, block_tables=bt)

@@ -41,7 +41,8 @@ def _prob(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(page_size=32), B.PA_ERR_UNSUPPORTED),
     (dict(head_dim=64), B.PA_ERR_UNSUPPORTED),
-    (dict(qlen=5, q_per_kv=8), B.PA_ERR_UNSUPPORTED),
+    (dict(qlen=9, q_per_kv=8), B.PA_ERR_UNSUPPORTED),  # 72 query rows per KV head
+    (dict(qlen=5, q_per_kv=8, head_dim=256), B.PA_ERR_UNSUPPORTED),  # 40 rows at head_dim 256
     (dict(num_blocks=0), B.PA_ERR_INVALID_ARG),
     (dict(qlen=0), B.PA_ERR_INVALID_ARG),
     (dict(kv_dtype="fp8"), B.PA_ERR_INVALID_ARG),  # fp8 without scales
@@ -62,6 +63,16 @@ def test_refusals(kw, status):
         B.pa_plan_host(_prob(**kw), [10, 20, 30, 40])
     assert ei.value.status == status
     assert B.pa_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(qlen=4, q_per_kv=16), dict(qlen=5, q_per_kv=8), dict(qlen=2, q_per_kv=16),
+                                dict(qlen=4, q_per_kv=8, head_dim=256), dict(qlen=8, q_per_kv=8, page_size=128)])
+def test_row_counts_up_to_64_are_planned(kw):
+    """Up to 64 query rows per KV head at head_dim 128 (ROCm/aiter PR #7092,
+    "Tests": the (qlen 4, one KV head, GQA 16, head_dim 128) case), up to 32
+    at head_dim 256."""
+    tasks, parts, info = B.pa_plan_host(_prob(**kw), [10, 20, 300, 600])
+    assert info.num_tasks > 0
 
 
 @pytest.mark.parametrize("kw,status", [

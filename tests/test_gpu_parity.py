@@ -7,6 +7,8 @@ the NaN contract: output finite and bit-identical between runs whose unowned
 rows are zero-filled and runs where they hold NaN / Inf / random bytes
 (ROCm/aiter PR #7092, section "Tests"), and bit-identical across repeated runs.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -282,3 +284,63 @@ def test_mxfp4_refuses_a_window():
     with pytest.raises(B.PaError) as ei:
         B.pa_plan(B.problem_of(case, window=128), case.context_lens)
     assert ei.value.status == B.PA_ERR_UNSUPPORTED
+
+
+WINDOW_SPECS = [s for s in GPU_MASK_SPECS if s.window > 0]
+
+
+def _decode_modes(case):
+    """The planned decode (automatic and split into many partitions) and the
+    plan-free decode of a case."""
+    return {"auto": run(case)[0], "many": run(case, task_budget=100000)[0], "direct": run_direct(case)}
+
+
+@pytest.mark.parametrize("spec", WINDOW_SPECS, ids=lambda s: s.name)
+def test_prewindow_rows_and_columns_are_inert(spec):
+    """A caller that frees the pages a sliding window has left behind points
+    their table columns at block 0 and leaves garbage in the earlier rows of
+    the window's first page. Those rows and their per-token scales hold NaN,
+    Inf or random bytes here; the output must stay finite and bit-identical to
+    the zero-filled run with the original table (ROCm/aiter PR #7092, "Tests":
+    the wider probe's sliding-window shapes under NaN / Inf / random fills)."""
+    case = I.make_case(spec, fill="zero")
+    base = _decode_modes(case)
+    ref = oracle.pa_decode(case)
+    for fill in ("nan", "inf", "random"):
+        pc = I.poison_prewindow(case, fill)
+        got = _decode_modes(pc)
+        for mode, out in got.items():
+            assert torch.isfinite(out.float()).all(), "%s %s: non-finite output" % (fill, mode)
+            assert torch.equal(out.view(torch.int16), base[mode].view(torch.int16)), \
+                "%s %s: pre-window fill changes the output" % (fill, mode)
+    check_parity(base["auto"], ref, what=spec.name)
+
+
+@pytest.mark.slow
+def test_prewindow_rows_are_inert_at_full_size():
+    """The same contract on the full-size 1024-token window workload."""
+    case = I.make_case(I.BF16_P64_W1024, fill="zero")
+    base = run(case)[0]
+    for fill in ("nan", "random"):
+        out = run(I.poison_prewindow(case, fill))[0]
+        assert torch.isfinite(out.float()).all()
+        assert torch.equal(out.view(torch.int16), base.view(torch.int16)), fill
+
+
+@pytest.mark.parametrize("spec", [s for s in WINDOW_SPECS if s.name in (
+    "g_bf16_q2_win", "g_fp8tok_q4_causal_win", "g_fp8trans_win", "g_fp8tok_d256_p128_q4_causal_win")],
+    ids=lambda s: s.name)
+def test_window_plan_with_shorter_device_lengths(spec):
+    """A plan made from host lengths, decoded with shorter device lengths: the
+    device window starts earlier than the planned one, and its tiles must
+    still be read (pa_plan: device lengths may be equal or shorter)."""
+    case = I.make_case(spec)
+    host = case.context_lens.clone()
+    for cut in (1, 37, 300, 1000):
+        short = dataclasses.replace(case, context_lens=(host - cut).clamp(min=0).to(torch.int32))
+        ref = oracle.pa_decode(short)
+        for over in ({}, {"task_budget": 100000}):
+            plan = B.pa_plan(B.problem_of(case, **over), host)
+            out, _ = B.decode_case(short, plan=plan)
+            torch.cuda.synchronize()
+            check_parity(out, ref, what="%s cut %d %s" % (spec.name, cut, over))

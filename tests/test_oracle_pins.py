@@ -481,3 +481,19 @@ def test_empty_causal_rows_are_zero():
     case = I.make_case(MASK_SPECS[0])  # L = 1 with qlen 4
     got = oracle.pa_decode(case)
     assert np.all(got[0, :3] == 0) and np.any(got[0, 3] != 0)
+
+
+@pytest.mark.parametrize("spec", MASK_SPECS[1:4], ids=lambda s: s.name)
+def test_prewindow_poison_is_invisible_to_the_oracle(spec):
+    """Freeing what every row's window has left behind (table columns wholly
+    before it pointed at block 0, earlier rows of its first page filled with
+    NaN / Inf / random bytes and scales) leaves the decode unchanged: the
+    definition reads only positions inside some row's range."""
+    case = I.make_case(spec.replace(lens=("fixed", tuple(L + 300 for L in spec.lens[1]))), fill="zero")
+    want = oracle.pa_decode(case)
+    moved = 0
+    for fill in ("nan", "inf", "random"):
+        pc = I.poison_prewindow(case, fill)
+        moved += int((pc.block_tables != case.block_tables).sum())
+        np.testing.assert_array_equal(oracle.pa_decode(pc), want)
+    assert moved > 0  # some table column lies wholly before a window
