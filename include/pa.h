@@ -226,6 +226,43 @@ pa_status pa_decode_direct(const pa_problem* problem, const void* query, const v
                            const int32_t* block_tables, const int32_t* context_lens, void* out, pa_stream_t stream);
 
 /*
+ * pa_decode_static -- pa_decode_direct's arguments, and a decode that
+ * allocates nothing and needs no plan: for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * Every sequence is split into the same number P of partitions of the tiles
+ * max_context_len (capped by max_blocks_per_seq * page_size, and with a window
+ * by the tiles its rows' windows can span) implies; partition p of a sequence
+ * covers its tiles [p * T, (p + 1) * T) counted from its window's first tile
+ * (the last partition also covers any tiles beyond), so device lengths may be
+ * anything up to the table's reach. The partials go to a static device buffer
+ * of PA_STATIC_SCRATCH_BYTES inside the library (one per GPU, held until the
+ * process ends), and the log-sum-exp merge kernel combines them; with P = 1
+ * each task writes its rows directly, exactly as pa_decode_direct does.
+ *
+ *   max_partitions 0   P is chosen for about one round of resident
+ *                      workgroups and lowered until the partials fit the buffer.
+ *   max_partitions > 0 P = min(max_partitions, tiles); if its partials
+ *                      (num_seqs * P * num_kv_heads * qlen * q_per_kv *
+ *                      (head_dim + 2) * 4 bytes, plus alignment) exceed the
+ *                      buffer, PA_ERR_UNSUPPORTED, before any device work.
+ *
+ * Every partial a call reads is written by the same call, so nothing needs
+ * clearing between calls; the buffer keeps the last call's partials. All
+ * calls on one GPU share the buffer: calls that overlap on a GPU (different
+ * streams, or threads without ordering) race and give undefined output, so
+ * keep them stream-ordered. Layouts, refusals and device-side guarantees are
+ * pa_decode's; task_budget is ignored. Nothing is allocated or synchronized;
+ * the first call on a device looks up the buffer's address there.
+ */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+
+pa_status pa_decode_static(const pa_problem* problem, const void* query, const void* key_cache,
+                           const void* value_cache, const void* k_scale, const void* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, void* out, pa_stream_t stream);
+
+/*
  * pa_write_kv_mxfp4 -- the MXFP4 KV-cache write: quantize num_tokens new K and V
  * rows and store them in the paged MXFP4 caches that pa_decode reads (ROCm/aiter
  * PR #7056, "Summary": the MXFP4 pages come from a separate KV-write kernel, as

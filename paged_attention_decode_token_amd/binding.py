@@ -56,7 +56,7 @@ class pa_mqa_problem(ctypes.Structure):
                                               "num_seqs", "max_blocks_per_seq", "out_stride")]
 
 
-EXPORTS = ["pa_plan", "pa_decode", "pa_decode_direct", "pa_write_kv_mxfp4", "pa_mqa_logits_mxfp4", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
+EXPORTS = ["pa_plan", "pa_decode", "pa_decode_direct", "pa_decode_static", "pa_write_kv_mxfp4", "pa_mqa_logits_mxfp4", "pa_plan_destroy", "pa_plan_workspace_bytes", "pa_plan_get_info",
            "pa_plan_host", "pa_plan_set_timing", "pa_plan_read_timing", "pa_last_error", "pa_version"]
 
 _lib = None
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.argtypes = [vp] * 10
     L.pa_decode_direct.restype = ctypes.c_int
     L.pa_decode_direct.argtypes = [P(pa_problem)] + [vp] * 9
+    L.pa_decode_static.restype = ctypes.c_int
+    L.pa_decode_static.argtypes = [P(pa_problem)] + [vp] * 9
     L.pa_write_kv_mxfp4.restype = ctypes.c_int
     L.pa_write_kv_mxfp4.argtypes = [P(pa_kv_write_problem)] + [vp] * 8
     L.pa_mqa_logits_mxfp4.restype = ctypes.c_int
@@ -253,6 +255,20 @@ def pa_decode_direct(problem: pa_problem, query, key_cache, value_cache, k_scale
     """Plan-free decode (one task per sequence and KV head); enqueued on `stream`."""
     _check_decode_sizes(problem, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, out)
     st = lib().pa_decode_direct(ctypes.byref(problem), _dev(query, "query"), _dev(key_cache, "key_cache"),
+                                _dev(value_cache, "value_cache"), _dev(k_scale, "k_scale", True),
+                                _dev(v_scale, "v_scale", True), _dev(block_tables, "block_tables"),
+                                _dev(context_lens, "context_lens"), _dev(out, "out"),
+                                ctypes.c_void_p(_stream_ptr(stream)))
+    _check(st)
+    return out
+
+
+def pa_decode_static(problem: pa_problem, query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                     context_lens, out, stream=None):
+    """Allocation-free decode (uniform partitions, partials in the library's
+    static device buffer); enqueued on `stream`."""
+    _check_decode_sizes(problem, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, out)
+    st = lib().pa_decode_static(ctypes.byref(problem), _dev(query, "query"), _dev(key_cache, "key_cache"),
                                 _dev(value_cache, "value_cache"), _dev(k_scale, "k_scale", True),
                                 _dev(v_scale, "v_scale", True), _dev(block_tables, "block_tables"),
                                 _dev(context_lens, "context_lens"), _dev(out, "out"),

@@ -481,7 +481,7 @@ pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_ca
     hipError_t e = hipSetDevice(plan->device);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "hipSetDevice failed: %s", hipGetErrorString(e));
 
-    pa::TileArgs a;
+    pa::TileArgs a{};
     a.q = query;
     a.k = key_cache;
     a.v = value_cache;
@@ -571,8 +571,144 @@ pa_status pa_decode_direct(const pa_problem* problem, const void* query, const v
     a.causal = p.causal;
     a.window = p.window;
     a.plan_free = 1;
+    a.uniform_parts = 1;
     e = pa::launch_tile(key, a, p.num_seqs * p.num_kv_heads, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "tile kernel launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------ allocation-free decode
+//
+// pa_decode_static keeps its partition partials in this array: one copy per
+// device, loaded with the library's code object and held until the process
+// ends. Host code never passes the array's name to a kernel or a copy (on the
+// host it is a stand-in, not a device address); the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static constexpr size_t kStaticScratchBytes = PA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device `dev`.
+pa_status static_scratch(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return PA_OK;
+}
+
+// Partial bytes of P partitions per sequence: (m, l) of every slot row, then
+// O, 256-byte aligned.
+size_t static_partial_bytes(const pa_problem& p, long P, size_t* o_off) {
+    const size_t n = (size_t)p.num_seqs * (size_t)P * (size_t)p.num_kv_heads * (size_t)rows_of(p);
+    const size_t ml = (n * 2 * sizeof(float) + 255) & ~size_t(255);
+    *o_off = ml;
+    return ml + n * (size_t)p.head_dim * sizeof(float);
+}
+
+// Tiles a sequence can span: the table's reach and max_context_len, and with a
+// window the tiles its rows' windows cover (at most W + qlen - 1 tokens).
+int static_tiles(const pa_problem& p) {
+    long reach = std::min<long>(p.max_context_len, (long)p.max_blocks_per_seq * p.page_size);
+    long tiles = (reach + pa::kTileTokens - 1) / pa::kTileTokens;
+    if (p.window > 0)
+        tiles = std::min<long>(tiles, ((long)p.window + p.qlen - 1 + pa::kTileTokens - 1) / pa::kTileTokens + 1);
+    return (int)std::max<long>(1, tiles);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_static(const pa_problem* problem, const void* query, const void* key_cache,
+                           const void* value_cache, const void* k_scale, const void* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, void* out, pa_stream_t stream) {
+    pa_status st = validate(problem);
+    if (st != PA_OK) return st;
+    const pa_problem& p = *problem;
+    if (p.num_seqs == 0) return PA_OK;
+    st = check_pointers(p, query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens, out);
+    if (st != PA_OK) return st;
+    const int tiles = static_tiles(p);
+    const long pairs = (long)p.num_seqs * p.num_kv_heads;
+    size_t o_off = 0;
+    int P = 0;
+    if (p.max_partitions > 0) {
+        P = std::min(p.max_partitions, tiles);
+        const size_t need = static_partial_bytes(p, P, &o_off);
+        if (P > 1 && need > kStaticScratchBytes)
+            return fail(PA_ERR_UNSUPPORTED,
+                        "%d partitions need %zu bytes of partials; the static scratch holds %zu (max_partitions 0 "
+                        "picks a count that fits)",
+                        P, need, kStaticScratchBytes);
+    }
+    DeviceInfo dev;
+    st = probe_device(&dev);
+    if (st != PA_OK) return st;
+    if (!dev.gfx950) return fail(PA_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 only", dev.device, dev.arch.c_str());
+    const pa::KernelKey key = key_of(p);
+    if (!pa::have_tile_kernel(key)) return fail(PA_ERR_UNSUPPORTED, "no kernel instance for this problem");
+    if (P == 0) {
+        // about one round of resident workgroups, as many partials as fit
+        const long slots = (long)dev.num_cus * pa::tile_blocks_per_cu(key);
+        P = (int)std::min<long>(std::min(64, tiles), std::max<long>(1, (slots + pairs - 1) / pairs));
+        while (P > 1 && static_partial_bytes(p, P, &o_off) > kStaticScratchBytes) --P;
+    }
+    const int part_tiles = (tiles + P - 1) / P;
+    P = (tiles + part_tiles - 1) / part_tiles;  // no partition left without tiles
+    if (pairs * P > 0x7FFFFFFFL) return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads * partitions exceeds the grid");
+    void* base = nullptr;
+    if (P > 1) {
+        st = static_scratch(dev.device, &base);
+        if (st != PA_OK) return st;
+        static_partial_bytes(p, P, &o_off);
+    }
+
+    pa::TileArgs a{};
+    a.q = query;
+    a.k = key_cache;
+    a.v = value_cache;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.part_ml = static_cast<float*>(base);
+    a.part_o = base ? reinterpret_cast<float*>(static_cast<char*>(base) + o_off) : nullptr;
+    a.num_seqs = p.num_seqs;
+    a.qlen = p.qlen;
+    a.num_kv_heads = p.num_kv_heads;
+    a.q_per_kv = p.q_per_kv;
+    a.rows = rows_of(p);
+    a.max_blocks = p.max_blocks_per_seq;
+    a.num_blocks = p.num_blocks;
+    const double sm = p.softmax_scale != 0.f ? (double)p.softmax_scale : 1.0 / std::sqrt((double)p.head_dim);
+    a.scale_log2 = (float)(sm * 1.4426950408889634);
+    a.causal = p.causal;
+    a.window = p.window;
+    a.plan_free = 1;
+    a.uniform_parts = P;
+    a.part_tiles = part_tiles;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = pa::launch_tile(key, a, (int)(pairs * P), s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "tile kernel launch failed: %s", hipGetErrorString(e));
+    if (P > 1) {
+        e = pa::launch_merge(a, p.head_dim, s);
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
+    }
     return PA_OK;
 }
 

@@ -32,7 +32,12 @@ struct TileArgs {
     float* part_o;             // [slots][Hkv][rows][D]: unnormalised weighted sum of V
     int32_t num_seqs, qlen, num_kv_heads, q_per_kv, rows, max_blocks, num_blocks;
     float scale_log2;  // softmax_scale * log2(e)
-    int32_t plan_free;  // 1: one task per (sequence, KV head) from the block index, tasks unused
+    int32_t plan_free;  // 1: tasks follow from the block index, the task list and seq_parts are unused:
+                        // uniform_parts tasks per (sequence, KV head), each part_tiles tiles
+                        // (the last open-ended); with more than one, partition p of sequence b
+                        // writes partial slot b * uniform_parts + p
+    int32_t uniform_parts;  // plan_free: partitions per sequence (0 or 1: direct output)
+    int32_t part_tiles;     // plan_free with uniform_parts > 1: tiles per partition
     int32_t causal;     // 1: query token i attends to t < L - qlen + i + 1
     int32_t window;     // > 0: and to t >= (that end) - window
 };

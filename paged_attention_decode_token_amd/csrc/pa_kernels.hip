@@ -981,15 +981,18 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     cx.lg = cx.lane >> 4;
     // A planned launch reads its task (sequence, KV head | partition << 16,
     // tile range) from the plan; a plan-free launch derives it from the block
-    // index: one task per (sequence, KV head) over all of its tiles, stored
-    // directly (PR #7056, "Bandwidth": tasks follow from the block index).
+    // index (PR #7056, "Bandwidth": tasks follow from the block index): one
+    // task per (sequence, KV head) over all of its tiles, stored directly, or
+    // `uniform_parts` tasks of `part_tiles` tiles each, partition fastest.
     int part, tb, te_task;
     if (a.plan_free) {
-        cx.b = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
-        cx.kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
-        part = 0;
-        tb = 0;
-        te_task = 0x7FFFFFFF;
+        const unsigned P = a.uniform_parts > 1 ? (unsigned)a.uniform_parts : 1u;
+        const unsigned g = blockIdx.x / P;
+        part = (int)(blockIdx.x % P);
+        cx.b = (int)(g / (unsigned)a.num_kv_heads);
+        cx.kvh = (int)(g % (unsigned)a.num_kv_heads);
+        tb = part * a.part_tiles;
+        te_task = (P == 1 || part == (int)P - 1) ? 0x7FFFFFFF : tb + a.part_tiles;
     } else {
         const int* task = a.tasks + 4 * blockIdx.x;
         cx.b = uniform(task[0]);
@@ -1004,7 +1007,6 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     L = L > a.max_blocks * PG ? a.max_blocks * PG : L;
     cx.L = L;
     const int ntiles = (L + kTileTokens - 1) / kTileTokens;
-    const int te = min(te_task, ntiles);
     cx.npages = (L + PG - 1) / PG;
     cx.bt_row = a.block_tables + (long)cx.b * a.max_blocks;
     const long head_bytes = C::PAGE_BYTES_HEAD;
@@ -1086,10 +1088,12 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     const int e_min = C::WIN ? max(0, a.causal ? L - a.qlen + 1 : L) : L;  // smallest row end
     const int s_min = C::WIN && a.window > 0 ? max(0, e_min - a.window) : 0;
     const int s_max = C::WIN && a.window > 0 ? max(0, L - a.window) : 0;
-    const int T0 = part == 0 ? s_min / kTileTokens : max(tb, s_min / kTileTokens);
+    // plan-free partitions count their tiles from the window's first tile
+    const int w0 = C::WIN && a.plan_free ? s_min / kTileTokens : 0;
+    const int T0 = part == 0 ? s_min / kTileTokens : max(tb + w0, s_min / kTileTokens);
     cx.s_lo = s_min;
     cx.pg_first = C::WIN ? min(s_min / PG, max(cx.npages - 1, 0)) : 0;
-    const int T1 = te;
+    const int T1 = te_task == 0x7FFFFFFF ? ntiles : min(te_task + w0, ntiles);
     const int F0 = max(T0, (s_max + kTileTokens - 1) / kTileTokens);
     const int F1 = max(F0, min(T1, e_min / kTileTokens));
     if constexpr (C::PF) {
@@ -1246,7 +1250,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] += *reinterpret_cast<f32x4*>(obuf_at(0, nt, dt));
 
-    const int nparts = a.plan_free ? 1 : a.seq_parts[2 * cx.b];
+    const int nparts = a.plan_free ? (a.uniform_parts > 1 ? a.uniform_parts : 1) : a.seq_parts[2 * cx.b];
     const int Hq = a.num_kv_heads * a.q_per_kv;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1263,7 +1267,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
                 *reinterpret_cast<u32x2*>(op + 2 * (16 * dt + 4 * cx.lg)) = w;
             }
         } else {
-            const long slot = (long)a.seq_parts[2 * cx.b + 1] + part;
+            const long slot = (a.plan_free ? (long)cx.b * nparts : (long)a.seq_parts[2 * cx.b + 1]) + part;
             const long prow = (slot * a.num_kv_heads + cx.kvh) * a.rows + r;
             float* po = a.part_o + prow * D;
 #pragma unroll
@@ -1306,9 +1310,9 @@ __global__ __launch_bounds__(256) void pa_merge_kernel(const TileArgs a) {
     const int i = rem / Hq, h = rem % Hq;
     const int kvh = h / a.q_per_kv;
     const int r = i * a.q_per_kv + h % a.q_per_kv;
-    const int P = a.seq_parts[2 * b];
+    const int P = a.plan_free ? a.uniform_parts : a.seq_parts[2 * b];
     if (P <= 1) return;
-    const long slot0 = a.seq_parts[2 * b + 1];
+    const long slot0 = a.plan_free ? (long)b * P : a.seq_parts[2 * b + 1];
     const long stride = (long)a.num_kv_heads * a.rows;  // rows between consecutive partitions
     const long prow0 = (slot0 * a.num_kv_heads + kvh) * a.rows + r;
     float m = -__builtin_inff(), l = 0.f;

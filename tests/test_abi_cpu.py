@@ -266,3 +266,16 @@ def test_planner_skips_tiles_before_the_window(window, causal):
                 mine = sorted((t[2], t[3]) for t in tasks.tolist() if t[0] == b and (t[1] & 0xFFFF) == kvh)
                 covered = [x for t0, t1 in mine for x in range(t0, t1)]
                 assert covered == list(range(min(first, ntiles), ntiles)), (b, L, mine)
+
+
+def test_static_decode_refuses_partials_beyond_its_buffer_before_the_device():
+    """pa_decode_static with an explicit partition count whose partials do not
+    fit its static buffer is refused with PA_ERR_UNSUPPORTED before any device
+    call (so on a host without one too); the pointers are never touched."""
+    p = _prob(num_seqs=64, num_kv_heads=8, q_per_kv=8, max_context_len=64 * 256, max_blocks_per_seq=1100,
+              max_partitions=64)
+    fake = [B.ctypes.c_void_p(0x100000 + 0x1000 * i) for i in range(9)]
+    st = B.lib().pa_decode_static(B.ctypes.byref(p), *fake)
+    assert st == B.PA_ERR_UNSUPPORTED
+    msg = B.pa_last_error()
+    assert "static scratch" in msg and "partitions" in msg, msg

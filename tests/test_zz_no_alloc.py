@@ -1,0 +1,123 @@
+"""The allocation-free decode, pa_decode_static, through the C ABI.
+
+Its output is checked against pa_decode's (the planned decode, whose plan owns
+its workspace) on the same inputs, to the parity bar: rel-L2 <= 3e-3 and
+|err| <= 2e-2 * max(1, |ref|) per element, with pa_decode's output as the
+reference; and against the fp64 oracle to the same bar. Two calls run back to
+back, the second on a smaller problem, so the second reads only partials its
+own call wrote into the library's static buffer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_attention_decode_token_amd import binding as B
+from paged_attention_decode_token_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 3e-3
+ELEM = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+
+
+def _bar(got, ref, what):
+    g = got.float().cpu().double().numpy()
+    r = ref if isinstance(ref, np.ndarray) else ref.float().cpu().double().numpy()
+    assert np.isfinite(g).all(), "%s: non-finite output" % what
+    err = g - r
+    nrm = np.linalg.norm(r)
+    rel = np.linalg.norm(err) / nrm if nrm > 0 else np.linalg.norm(err)
+    worst = float((np.abs(err) / (ELEM * np.maximum(1.0, np.abs(r)))).max()) if err.size else 0.0
+    print("%s: rel-L2 %.3e, worst |err|/bound %.3f" % (what, rel, worst))
+    assert rel <= REL_L2 and worst <= 1.0, what
+
+
+def _out(case):
+    return torch.full((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), float("nan"),
+                      dtype=torch.bfloat16, device="cuda")
+
+
+def _static(case, d, **over):
+    out = _out(case)
+    B.pa_decode_static(B.problem_of(case, **over), d["query"], d["key_cache"], d["value_cache"], d["k_scale"],
+                       d["v_scale"], d["block_tables"], d["context_lens"], out)
+    return out
+
+
+def _planned(case, d):
+    out = _out(case)
+    plan = B.pa_plan(B.problem_of(case), case.context_lens)
+    B.pa_decode(plan, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
+                d["block_tables"], d["context_lens"], out)
+    torch.cuda.synchronize()
+    return out
+
+
+PAIRS = [
+    # (first call, second smaller call)
+    (I.Spec("na_bf16_big", 6, ("fixed", (3000, 2100, 1, 777, 2900, 1500)), 1, 2, 8, 128, 64, "bf16", seed=70),
+     I.Spec("na_bf16_small", 2, ("fixed", (300, 1000)), 1, 1, 8, 128, 64, "bf16", seed=71)),
+    (I.Spec("na_fp8tok_q4", 3, ("fixed", (2400, 200, 1900)), 4, 2, 8, 256, 16, "fp8", "token", seed=72),
+     I.Spec("na_fp8tok_q1", 2, ("fixed", (17, 900)), 1, 1, 8, 256, 16, "fp8", "token", seed=73)),
+    (I.Spec("na_mxfp4", 3, ("fixed", (1, 3000, 2048)), 1, 2, 16, 128, 128, "mxfp4", q_dtype="bf16", seed=74),
+     I.Spec("na_mxfp4_small", 1, ("fixed", (600,)), 1, 1, 16, 128, 128, "mxfp4", q_dtype="fp8", seed=75)),
+    (I.Spec("na_fp8trans_causal_win", 3, ("fixed", (3000, 700, 2500)), 4, 1, 16, 128, 128, "fp8", "tensor", "trans",
+            seed=76, causal=1, window=900),
+     I.Spec("na_bf16_win", 2, ("fixed", (1300, 40)), 2, 1, 4, 128, 16, "bf16", seed=77, window=300)),
+]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: p[0].name)
+def test_static_decode_matches_planned_decode_two_calls(pair):
+    outs = []
+    for spec in pair:
+        case = I.make_case(spec)
+        d = B.device_tensors(case)
+        got = _static(case, d)
+        torch.cuda.synchronize()
+        outs.append((case, d, got))
+    # checked after both calls ran: the second call's partials overwrote the first's
+    for case, d, got in outs:
+        ref = _planned(case, d)
+        _bar(got, ref, case.spec.name + " vs pa_decode")
+        _bar(got, oracle.pa_decode(case), case.spec.name + " vs oracle")
+        for fill in ("nan", "random"):
+            dp = B.device_tensors(I.refill(case, fill))
+            assert torch.equal(_static(case, dp).view(torch.int16), got.view(torch.int16)), fill
+
+
+@pytest.mark.parametrize("max_partitions", [1, 3, 64])
+def test_static_decode_explicit_partitions(max_partitions):
+    """max_partitions 1 is the plan-free decode bit for bit; other counts stay
+    within the bar of pa_decode."""
+    case = I.make_case(PAIRS[0][0])
+    d = B.device_tensors(case)
+    got = _static(case, d, max_partitions=max_partitions)
+    torch.cuda.synchronize()
+    if max_partitions == 1:
+        direct = _out(case)
+        B.pa_decode_direct(B.problem_of(case), d["query"], d["key_cache"], d["value_cache"], d["k_scale"],
+                           d["v_scale"], d["block_tables"], d["context_lens"], direct)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), direct.view(torch.int16))
+    _bar(got, _planned(case, d), "max_partitions %d vs pa_decode" % max_partitions)
+
+
+def test_static_decode_allocates_nothing_through_torch():
+    case = I.make_case(PAIRS[1][0])
+    d = B.device_tensors(case)
+    out = _out(case)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_stats()["allocation.all.allocated"]
+    for _ in range(3):
+        B.pa_decode_static(B.problem_of(case), d["query"], d["key_cache"], d["value_cache"], d["k_scale"],
+                           d["v_scale"], d["block_tables"], d["context_lens"], out)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_stats()["allocation.all.allocated"] == before
