@@ -19,8 +19,7 @@ from paged_attention_decode_token_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-REL_L2 = 3e-3
-ELEM = 2e-2
+from parity_bar import REL_L2, check_parity  # noqa: F401  (the bar, shared with its CPU controls)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -31,22 +30,6 @@ def _gpu():
 
 def _bits(t):
     return t.view(torch.int16).cpu().numpy()
-
-
-def check_parity(gpu_out, ref, seqs=None, what=""):
-    g = gpu_out.float().cpu().double().numpy()
-    if seqs is not None:
-        g, ref = g[seqs], ref[seqs]
-    assert np.isfinite(g).all(), "%s: non-finite output" % what
-    err = g - ref
-    nrm = np.linalg.norm(ref)
-    rel = np.linalg.norm(err) / nrm if nrm > 0 else np.linalg.norm(err)
-    bound = ELEM * np.maximum(1.0, np.abs(ref))
-    worst = float((np.abs(err) / bound).max()) if err.size else 0.0
-    print("%s: rel-L2 %.3e, worst |err|/bound %.3f" % (what, rel, worst))
-    assert rel <= REL_L2, "%s: rel-L2 %.3e > %.1e" % (what, rel, REL_L2)
-    assert worst <= 1.0, "%s: element error %.3f x bound" % (what, worst)
-    return rel
 
 
 def run(case, **over):

@@ -17,7 +17,8 @@ import oracle
 from paged_attention_decode_token_amd import binding as B
 from paged_attention_decode_token_amd import inputs as I
 
-from test_gpu_parity import check_parity, run, run_direct
+from parity_bar import check_parity
+from test_gpu_parity import run, run_direct
 
 pytestmark = pytest.mark.gpu
 

@@ -17,8 +17,7 @@ from paged_attention_decode_token_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-REL_L2 = 3e-3
-ELEM = 2e-2
+from parity_bar import parity_stats
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,15 +27,11 @@ def _gpu():
 
 
 def _bar(got, ref, what):
-    g = got.float().cpu().double().numpy()
+    """The parity bar with `ref` (an fp64 array, or another decode's output) as the reference."""
     r = ref if isinstance(ref, np.ndarray) else ref.float().cpu().double().numpy()
-    assert np.isfinite(g).all(), "%s: non-finite output" % what
-    err = g - r
-    nrm = np.linalg.norm(r)
-    rel = np.linalg.norm(err) / nrm if nrm > 0 else np.linalg.norm(err)
-    worst = float((np.abs(err) / (ELEM * np.maximum(1.0, np.abs(r)))).max()) if err.size else 0.0
+    rel, worst, finite = parity_stats(got, r)
     print("%s: rel-L2 %.3e, worst |err|/bound %.3f" % (what, rel, worst))
-    assert rel <= REL_L2 and worst <= 1.0, what
+    assert finite and rel <= 3e-3 and worst <= 1.0, what
 
 
 def _out(case):
