@@ -199,6 +199,20 @@ def read_bytes(case) -> int:
     return toks * case.num_kv_heads * case.kv_bytes_per_token_head()
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo) and its logical CPU count."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return "%s (%d logical CPUs visible)" % (name, os.cpu_count() or 0)
+
+
 def time_cpu_oracle(case, target_s=15.0):
     import oracle
 
@@ -218,55 +232,74 @@ def time_cpu_oracle(case, target_s=15.0):
             break
     nbytes = case.kv_bytes(seqs) * reps
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d of %d sequences of the page-64 variant, %d passes (%.0f MB of KV), %.1f s" % (
                 n, case.num_seqs, reps, nbytes / 1e6, dt)}
 
 
-def time_all(steps, warmup, names=None):
-    """Per workload: cold-cache median us per pa_decode call, and the tile / merge
-    kernel split from the library's events (inputs resident in HBM).
+# The workloads of the decode's five configurations, timed per call by default.
+PER_CONFIG = [("cfg1", "TINY_BF16"), ("cfg2", "BF16_P64"), ("cfg2", "BF16_P128"), ("cfg3", "FP8TOK_Q1"),
+              ("cfg3", "FP8TOK_Q4"), ("cfg4", "FP8_TRANS"), ("cfg5a", "MXFP4_SHORT_Q8"), ("cfg5a", "MXFP4_SHORT_QBF"),
+              ("cfg5b", "MXFP4_LONG_Q8"), ("cfg5b", "MXFP4_LONG_QBF")]
+# and the MXFP4 ones again with the opt-in block-scaled fp4 x fp8 QK MFMA
+PER_CONFIG_SCALED_QK = ("MXFP4_SHORT_Q8", "MXFP4_SHORT_QBF", "MXFP4_LONG_Q8", "MXFP4_LONG_QBF")
 
-    Each event pair also brackets the event packets' own queue time (a few us,
-    which is a tenth of a 60 us call). So a second, differential figure is taken
-    too: `steps` cold calls (flush, call, flush, call, ...) between two events,
-    minus `steps` flushes alone between two events, divided by `steps` (median
-    of five alternating pairs of batches)."""
+
+def time_case(case, steps, warmup, flush, flush_out, extras=False, **problem_over):
+    """Cold-cache timing of pa_decode on one case (inputs resident in HBM).
+
+    Before each call a 1 GiB buffer is read (the last-level cache is 256 MB; a
+    read leaves clean lines, where a write would leave dirty lines for the
+    decode to write back); the median of the per-call event times is kept. The
+    tile / merge split comes from the library's own events around each kernel,
+    in a separate pass of the same calls. With `extras`, also the differential
+    figure (see time_all) and the plan-free pa_decode_direct's cold median."""
     import statistics
 
     import torch
 
     import paged_attention_decode_token_amd as pa
-    from paged_attention_decode_token_amd import inputs as I
 
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB last-level cache
-    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
-    rows = {}
-    specs = I.FULL if not names else [I.BY_NAME[n] for n in names]
-    for spec in specs:
-        case = I.make_case(spec)
-        d = pa.device_tensors(case)
-        plan = pa.pa_plan(pa.problem_of(case), case.context_lens)
-        out = torch.empty((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
-                          device="cuda")
+    d = pa.device_tensors(case)
+    plan = pa.pa_plan(pa.problem_of(case, **problem_over), case.context_lens)
+    out = torch.empty((case.num_seqs, case.qlen, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
 
-        def call():
-            pa.pa_decode(plan, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
-                         d["block_tables"], d["context_lens"], out)
+    def call():
+        pa.pa_decode(plan, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
+                     d["block_tables"], d["context_lens"], out)
 
+    def cold_median(fn):
         for _ in range(warmup):
-            call()
+            fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in ev:
             torch.amax(flush, dim=0, out=flush_out)  # read-only sweep of the flush buffer
             a.record()
-            call()
+            fn()
             b.record()
         torch.cuda.synchronize()
-        us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+        return statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+
+    us = cold_median(call)
+    plan.set_timing(True, steps)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    t_ms, m_ms, n = plan.read_timing()
+    plan.set_timing(False)
+    nbytes = read_bytes(case)
+    inf = plan.info()
+    gbps = nbytes / (us * 1e-6) / 1e9
+    row = {"us_per_call": round(us, 2), "kv_bytes": nbytes, "kv_GBps": round(gbps, 1),
+           "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1), "tile_us": round(t_ms / n * 1e3, 2),
+           "merge_us": round(m_ms / n * 1e3, 2) if inf.merge_needed else 0.0,
+           "tasks": inf.num_tasks, "slots": inf.slots, "partitions_max": inf.max_parts}
+    if extras:
         # differential cold time: the event packets' cost is paid once per batch;
         # batches with and without the calls alternate, and the median of five
         # differences is kept (the flushes alone vary by about 1 % between batches)
-        a, b = ev[0]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         diffs = []
         for _ in range(5):
             a.record()
@@ -283,45 +316,77 @@ def time_all(steps, warmup, names=None):
             torch.cuda.synchronize()
             diffs.append((t_calls - a.elapsed_time(b)) * 1e3 / steps)
         us_diff = statistics.median(diffs)
-        prob = pa.problem_of(case)
+        prob = pa.problem_of(case, **problem_over)
 
         def call_direct():
             pa.pa_decode_direct(prob, d["query"], d["key_cache"], d["value_cache"], d["k_scale"], d["v_scale"],
                                 d["block_tables"], d["context_lens"], out)
 
-        for _ in range(warmup):
-            call_direct()
-        for a, b in ev:
-            torch.amax(flush, dim=0, out=flush_out)
-            a.record()
-            call_direct()
-            b.record()
-        torch.cuda.synchronize()
-        us_direct = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
-        plan.set_timing(True, steps)
-        for _ in range(steps):
-            call()
-        torch.cuda.synchronize()
-        t_ms, m_ms, n = plan.read_timing()
-        plan.set_timing(False)
-        nbytes = read_bytes(case)
-        inf = plan.info()
-        gbps = nbytes / (us * 1e-6) / 1e9
-        rows[spec.name] = {"us_per_call": round(us, 2), "us_per_call_differential": round(us_diff, 2),
-                           "pct_of_hbm_peak_differential": round(100 * nbytes / (us_diff * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                           "tile_us": round(t_ms / n * 1e3, 2),
-                           "merge_us": round(m_ms / n * 1e3, 2) if inf.merge_needed else 0.0,
-                           "kv_bytes": nbytes, "kv_GBps": round(gbps, 1),
-                           "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 1),
-                           "tasks": inf.num_tasks, "slots": inf.slots, "partitions_max": inf.max_parts,
-                           "plan_free_us_per_call": round(us_direct, 2),
-                           "plan_free_pct_of_hbm_peak": round(100 * nbytes / (us_direct * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        us_direct = cold_median(call_direct)
+        row.update({"us_per_call_differential": round(us_diff, 2),
+                    "pct_of_hbm_peak_differential": round(100 * nbytes / (us_diff * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                    "plan_free_us_per_call": round(us_direct, 2),
+                    "plan_free_pct_of_hbm_peak": round(100 * nbytes / (us_direct * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)})
+    del d, plan, out
+    torch.cuda.empty_cache()
+    return row
+
+
+def time_per_config(steps, warmup):
+    """The default line's per-configuration block: every workload of the five
+    configurations, cold median us per pa_decode call, KV GB/s, % of 8 TB/s and
+    the tile / merge split."""
+    import torch
+
+    from paged_attention_decode_token_amd import inputs as I
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB last-level cache
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+    rows = {}
+    for cfg, attr in PER_CONFIG:
+        spec = getattr(I, attr)
+        case = I.make_case(spec)
+        variants = [("", {})] + ([("_scaled_qk", {"mxfp4_scaled_qk": 1})] if attr in PER_CONFIG_SCALED_QK else [])
+        for suffix, over in variants:
+            row = {"config": cfg}
+            row.update(time_case(case, steps, warmup, flush, flush_out, **over))
+            rows[spec.name + suffix] = row
+            print("%-6s %-42s %9.2f us  %7.1f GB/s  %5.1f%%  tile %8.2f us  merge %6.2f us" % (
+                cfg, spec.name + suffix, row["us_per_call"], row["kv_GBps"], row["pct_of_hbm_peak"], row["tile_us"],
+                row["merge_us"]), file=sys.stderr, flush=True)
+        del case
+    del flush
+    torch.cuda.empty_cache()
+    return rows
+
+
+def time_all(steps, warmup, names=None):
+    """Per workload: cold-cache median us per pa_decode call, and the tile / merge
+    kernel split from the library's events (inputs resident in HBM).
+
+    Each event pair also brackets the event packets' own queue time (a few us,
+    which is a tenth of a 60 us call). So a second, differential figure is taken
+    too: `steps` cold calls (flush, call, flush, call, ...) between two events,
+    minus `steps` flushes alone between two events, divided by `steps` (median
+    of five alternating pairs of batches)."""
+    import torch
+
+    from paged_attention_decode_token_amd import inputs as I
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB last-level cache
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+    rows = {}
+    specs = I.FULL if not names else [I.BY_NAME[n] for n in names]
+    for spec in specs:
+        case = I.make_case(spec)
+        row = time_case(case, steps, warmup, flush, flush_out, extras=True)
+        rows[spec.name] = row
         print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  differential %8.2f us %5.1f%%  tile %8.2f us  tasks %5d slots %4d  "
-              "plan-free %8.2f us" % (spec.name, us, gbps, 100 * gbps / HBM_PEAK_GBS, us_diff,
-                                      100 * nbytes / (us_diff * 1e-6) / 1e9 / HBM_PEAK_GBS, t_ms / n * 1e3,
-                                      inf.num_tasks, inf.slots, us_direct), file=sys.stderr, flush=True)
-        del d, plan, out, case
-        torch.cuda.empty_cache()
+              "plan-free %8.2f us" % (spec.name, row["us_per_call"], row["kv_GBps"], row["pct_of_hbm_peak"],
+                                      row["us_per_call_differential"], row["pct_of_hbm_peak_differential"],
+                                      row["tile_us"], row["tasks"], row["slots"], row["plan_free_us_per_call"]),
+              file=sys.stderr, flush=True)
+        del case
     return rows
 
 
@@ -432,6 +497,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-configuration cold per-call block of the default line")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload (one pa_decode call each) and print a table to stderr")
     ap.add_argument("--kv-write", action="store_true",
@@ -550,9 +617,10 @@ def main():
                      "timing": "library HIP events around each tile launch, second pass of the timed steps "
                                "(%.4f ms per step with the events)" % ms_instr},
     }
-    if args.all or args.kv_write or args.mqa:
-        del variants
-        torch.cuda.empty_cache()
+    del variants
+    torch.cuda.empty_cache()
+    if not args.no_per_config:
+        res["per_config"] = time_per_config(args.steps, args.warmup)
     if args.all:
         res["all_workloads"] = time_all(args.steps, args.warmup,
                                         [w for w in args.workloads.split(",") if w] or None)

@@ -172,11 +172,13 @@ struct Cfg {
     static constexpr int PG = PG_;
     static constexpr int NT = NT_;  // 16-row N tiles of query rows (rows <= 16 * NT)
     static constexpr bool QF8 = QF8_ != 0;
-    // MXFP4 QK on the block-scaled fp4 x fp8 MFMA (fast) instead of exact
+    // MXFP4 QK on the block-scaled fp4 x fp8 MFMA (opt-in) instead of exact
     // widening of K to bf16 and the bf16 MFMA (default). On gfx950 the scaled
-    // instruction sums some operand mixes to only about 2^-13 of their largest
-    // product, which near-tied logits turn into output errors above the
-    // element bound; the widened form is exact up to fp32 accumulation.
+    // instruction keeps one 32-element block's sum to about 2^-14 of the
+    // block's largest product (2^-12.6 with the query scaled up to 448),
+    // however the 128-deep reduction is split across instructions; near-tied
+    // logits can turn that into output errors above the element bound. The
+    // widened form is exact up to fp32 accumulation.
     static constexpr bool MXS = KV_ == KV_MXFP4 && MXS_ != 0;
     // P enters PV as bf16 hi + lo parts (two MFMAs) for MXFP4: its softmax is
     // near one-hot and its V rows reach 6 * 2^9, so bf16 rounding of a
