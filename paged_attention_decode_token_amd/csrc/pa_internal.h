@@ -26,16 +26,17 @@ struct TileArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     void* out;                 // bf16 [B][qlen][Hq][D]
-    const int32_t* tasks;      // int32 x 4 per task
-    const int32_t* seq_parts;  // int32 x 2 per sequence: partitions, first partial slot
-    float* part_ml;            // [slots][Hkv][rows][2]: running max (base 2), sum of weights
-    float* part_o;             // [slots][Hkv][rows][D]: unnormalised weighted sum of V
+    const int32_t* tasks;      // int32 x 4 per task, in workgroup order
+    const int32_t* seg_off;    // tasks [seg_off[w], seg_off[w + 1]) of workgroup w, or null: task w
+    const int32_t* seq_parts;  // int32 x 2 per (sequence, KV head): partitions, first partial unit
+    float* part_ml;            // [units][rows][2]: running max (base 2), sum of weights
+    float* part_o;             // [units][rows][D]: weighted sum of V (times the per-tensor V scale)
     int32_t num_seqs, qlen, num_kv_heads, q_per_kv, rows, max_blocks, num_blocks;
     float scale_log2;  // softmax_scale * log2(e)
     int32_t plan_free;  // 1: tasks follow from the block index, the task list and seq_parts are unused:
                         // uniform_parts tasks per (sequence, KV head), each part_tiles tiles
-                        // (the last open-ended); with more than one, partition p of sequence b
-                        // writes partial slot b * uniform_parts + p
+                        // (the last open-ended); with more than one, partition p of
+                        // (sequence b, KV head h) writes partial unit (b Hkv + h) uniform_parts + p
     int32_t uniform_parts;  // plan_free: partitions per sequence (0 or 1: direct output)
     int32_t part_tiles;     // plan_free with uniform_parts > 1: tiles per partition
     int32_t causal;     // 1: query token i attends to t < L - qlen + i + 1
@@ -96,6 +97,9 @@ hipError_t launch_merge(const TileArgs& args, int head_dim, hipStream_t stream);
 
 // Whether an instance exists for `key`.
 bool have_tile_kernel(const KernelKey& key);
+
+// Whether the instance for `key` runs a list of tasks per workgroup (seg_off).
+bool tile_runs_segments(const KernelKey& key);
 
 // Tile-kernel workgroups of `key` that fit on one compute unit at once.
 int tile_blocks_per_cu(const KernelKey& key);

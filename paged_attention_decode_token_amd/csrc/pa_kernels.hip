@@ -188,11 +188,12 @@ struct Cfg {
     // sum cannot share its rounding, so one bf16 rounding adds about 2^-9 / 3
     // of relative error per weight on top of the bf16 output rounding (rel-L2
     // 2.95e-3 against a 2.30e-3 output-rounding floor on 64 rows of a mixed
-    // short-length batch); hi + lo leaves only the output rounding. Not at
-    // head_dim 256 with 32 query rows, where the low parts' registers make the
-    // register-staged loop spill; one rounding there gives rel-L2 2.4e-3 on
-    // the qlen-4 batch against a 1.7e-3 floor.
-    static constexpr bool PSPLIT = KV == KV_MXFP4 || (SC_ == SC_TOKEN && !(NT_ == 2 && D_ == 256));
+    // short-length batch); hi + lo leaves only the output rounding. Only with
+    // 64 query rows: at 16 and 32 rows the second P*V product costs time (1 us
+    // of a 63 us tile kernel at 16 rows) or registers (the head_dim-256 loop
+    // spills at 32 rows), and one rounding gives rel-L2 2.4e-3 on the fp8
+    // per-token batch against a 1.7e-3 floor.
+    static constexpr bool PSPLIT = KV == KV_MXFP4 || (SC_ == SC_TOKEN && NT_ == 4);
     static constexpr int ESZ = KV == KV_BF16 ? 2 : 1;                // bytes per bf16/fp8 element
     static constexpr int ROWB = KV == KV_MXFP4 ? D / 2 : D * ESZ;    // bytes of one token row (data)
     static constexpr int SROWB = KV == KV_MXFP4 ? D / 32 : 0;        // bytes of one token's e8m0 scales
@@ -255,7 +256,9 @@ struct Cfg {
     static constexpr int VSTAGE_BYTES = VDMA ? 64 * ROWB : (STAGE_V ? 32 * VPITCH : 0);  // per wave
     static constexpr int SCALE_BYTES = PF ? 512 : 0;                 // K then V scales of 64 tokens (fp32)
     static constexpr int WAVE_LDS = (PF ? 2 : 1) * (VSTAGE_BYTES + SCALE_BYTES);  // per wave
-    static constexpr int QLDS_BYTES = QLDS ? NT * KSTEPS * 64 * 16 : 0;
+    // query fragments in LDS: one copy per workgroup (QLDS), or the next task's
+    // query, brought by LDS DMA while the current task streams (PF)
+    static constexpr int QLDS_BYTES = (QLDS || PF) ? NT * KSTEPS * 64 * 16 : 0;
     static constexpr int ROWS_PAD = 16 * NT;
     static constexpr int OPITCH = D + 4;                             // floats
     static constexpr int EPI_BYTES = 2 * ROWS_PAD * OPITCH * 4 + 2 * 4 * ROWS_PAD * 4;
@@ -794,6 +797,19 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
     }
 }
 
+// Workgroup barrier ordering LDS accesses only. __syncthreads also waits for
+// every outstanding global load, LDS DMA included; at a task switch that is
+// the next task's first stage, whose latency the merge is meant to overlap.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier (the barrier builtin alone does not order memory); the
+// wait makes this wave's LDS writes visible before it arrives.
+PA_DEV void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), the other counters untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 PA_DEV void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -971,22 +987,37 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
     }
 }
 
-template <class C>
-__global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const TileArgs a) {
-    constexpr int D = C::D, NT = C::NT, PG = C::PG;
-    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+// Tile range of one task: tiles [T0, T1) are read; [F0, F1) lie inside every
+// row's range and run unmasked.
+struct Range {
+    int T0, T1, F0, F1;
+};
 
-    Ctx cx;
-    cx.lane = threadIdx.x & 63;
-    cx.wave = uniform(threadIdx.x >> 6);
-    cx.ln = cx.lane & 15;
-    cx.lg = cx.lane >> 4;
-    // A planned launch reads its task (sequence, KV head | partition << 16,
-    // tile range) from the plan; a plan-free launch derives it from the block
-    // index (PR #7056, "Bandwidth": tasks follow from the block index): one
-    // task per (sequence, KV head) over all of its tiles, stored directly, or
-    // `uniform_parts` tasks of `part_tiles` tiles each, partition fastest.
-    int part, tb, te_task;
+// Set up task `idx` of the plan (plan-free: the task the block index names):
+// sequence, KV head, partition, the sequence's context and the tile range.
+//
+// A planned launch reads its task (sequence, KV head | partition << 16, tile
+// range) from the plan; a plan-free launch derives it from the block index
+// (PR #7056, "Bandwidth": tasks follow from the block index): one task per
+// (sequence, KV head) over all of its tiles, stored directly, or
+// `uniform_parts` tasks of `part_tiles` tiles each, partition fastest.
+//
+// Tiles of the task: the task's range cut to the tiles any row reads (from
+// the first row's window start to ceil(L / 256)). The first partition of a
+// (sequence, KV head) starts at the device window's first tile whatever the
+// plan says: a plan made from host lengths cuts the tiles before the host
+// window, and a shorter device length moves the window earlier (the other
+// partitions' ranges then still cover the rest). The window's first tiles and
+// the causal and context boundary at the end run the masked variant.
+// The task's own tile range before the cut, and the sequence's tile count.
+struct TaskTiles {
+    int tb, te, ntiles;
+};
+
+template <class C>
+PA_DEV TaskTiles task_read(const TileArgs& a, int idx, Ctx& cx, int& part) {
+    constexpr int PG = C::PG;
+    int tb, te_task;
     if (a.plan_free) {
         const unsigned P = a.uniform_parts > 1 ? (unsigned)a.uniform_parts : 1u;
         const unsigned g = blockIdx.x / P;
@@ -996,7 +1027,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
         tb = part * a.part_tiles;
         te_task = (P == 1 || part == (int)P - 1) ? 0x7FFFFFFF : tb + a.part_tiles;
     } else {
-        const int* task = a.tasks + 4 * blockIdx.x;
+        const int* task = a.tasks + 4 * idx;
         cx.b = uniform(task[0]);
         const int kp = uniform(task[1]);
         cx.kvh = kp & 0xFFFF;
@@ -1011,15 +1042,8 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     const int ntiles = (L + kTileTokens - 1) / kTileTokens;
     cx.npages = (L + PG - 1) / PG;
     cx.bt_row = a.block_tables + (long)cx.b * a.max_blocks;
-    const long head_bytes = C::PAGE_BYTES_HEAD;
-    cx.kbase = reinterpret_cast<const char*>(a.k) + (long)cx.kvh * head_bytes;
-    cx.vbase = reinterpret_cast<const char*>(a.v) + (long)cx.kvh * head_bytes;
-    cx.kscale = 1.f;
-    float vscale = 1.f;
-    if constexpr (C::SC == SC_TENSOR) {
-        cx.kscale = *reinterpret_cast<const float*>(a.ks);
-        vscale = *reinterpret_cast<const float*>(a.vs);
-    }
+    cx.kbase = reinterpret_cast<const char*>(a.k) + (long)cx.kvh * C::PAGE_BYTES_HEAD;
+    cx.vbase = reinterpret_cast<const char*>(a.v) + (long)cx.kvh * C::PAGE_BYTES_HEAD;
     if constexpr (C::SC == SC_TOKEN) {
         cx.ksbase = reinterpret_cast<const char*>(a.ks) + (long)cx.kvh * PG * 4;
         cx.vsbase = reinterpret_cast<const char*>(a.vs) + (long)cx.kvh * PG * 4;
@@ -1029,39 +1053,18 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
     } else {
         cx.ksbase = cx.vsbase = nullptr;
     }
+    return TaskTiles{tb, te_task, ntiles};
+}
 
-    QFrag<C> qf;
-    load_q<C>(a, cx, qf);
-
-    State<C> st;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        st.m[nt] = -__builtin_inff();
-        st.l[nt] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    char* vlds = smem + cx.wave * C::WAVE_LDS;
-    char* qlds = smem + 4 * C::WAVE_LDS;
-    if constexpr (C::QLDS) {
-        // one copy of the query fragments for the workgroup (the same for every wave)
-        if (cx.wave == 0) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int ks = 0; ks < C::KSTEPS; ++ks)
-                    *reinterpret_cast<u32x4*>(qlds + 16 * ((nt * C::KSTEPS + ks) * 64 + cx.lane)) =
-                        __builtin_bit_cast(u32x4, qf.q[nt][ks]);
-        }
-        __syncthreads();
-    }
-
+template <class C>
+PA_DEV Range task_range(const TileArgs& a, const TaskTiles& tt, Ctx& cx, int part) {
+    constexpr int PG = C::PG;
+    const int L = cx.L, tb = tt.tb, te_task = tt.te, ntiles = tt.ntiles;
     // Query row r of this lane (query token i = r / G) attends to
     // [row_s, row_e): e = L - qlen + i + 1 when causal, else L; s = e - window
     // with a sliding window, else 0.
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < C::NT; ++nt) {
         if constexpr (C::WIN) {
             const int r = 16 * nt + cx.ln;
             const int i = r < a.rows ? r / a.q_per_kv : a.qlen - 1;
@@ -1073,128 +1076,45 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
             cx.row_s[nt] = 0;
         }
     }
-    // Tiles of the task: [T0, T1), the task's range cut to the tiles any row
-    // reads (from the first row's window start to ceil(L / 256)). The first
-    // partition of a sequence starts at the device window's first tile
-    // whatever the plan says: a plan made from host lengths cuts the tiles
-    // before the host window, and a shorter device length moves the window
-    // earlier (the other partitions' ranges then still cover the rest). Tiles
-    // [F0, F1) lie inside every row's range and run unmasked; the others
-    // (the window's first tiles, the causal and context boundary at the end)
-    // run the masked variant. Loads run one stage ahead: V(j) is issued at
-    // the top of iteration j (right after PV(j - 1)), K(j + 1) right after
-    // QK(j). Every load of a loop is unconditional and each loop test comes
-    // after PV, so the waits before QK and PV cover exactly the loads of the
-    // current slice, never the prefetch in flight. The last tile runs after
-    // the loops with its own V loads, masked (a no-op on a full tile).
     const int e_min = C::WIN ? max(0, a.causal ? L - a.qlen + 1 : L) : L;  // smallest row end
     const int s_min = C::WIN && a.window > 0 ? max(0, e_min - a.window) : 0;
     const int s_max = C::WIN && a.window > 0 ? max(0, L - a.window) : 0;
     // plan-free partitions count their tiles from the window's first tile
     const int w0 = C::WIN && a.plan_free ? s_min / kTileTokens : 0;
-    const int T0 = part == 0 ? s_min / kTileTokens : max(tb + w0, s_min / kTileTokens);
     cx.s_lo = s_min;
     cx.pg_first = C::WIN ? min(s_min / PG, max(cx.npages - 1, 0)) : 0;
-    const int T1 = te_task == 0x7FFFFFFF ? ntiles : min(te_task + w0, ntiles);
-    const int F0 = max(T0, (s_max + kTileTokens - 1) / kTileTokens);
-    const int F1 = max(F0, min(T1, e_min / kTileTokens));
-    if constexpr (C::PF) {
-        if (T1 > T0) {
-            // stage = K (registers), V tile and scale block (LDS) of one slice;
-            // stage(tile + 1) is issued right after the wait for stage(tile)
-            using Masked = BoolTag<true>;
-            using Full = BoolTag<false>;
-            constexpr int BUF = C::VSTAGE_BYTES + C::SCALE_BYTES;
-            int cb = T0 * kTileTokens + 64 * cx.wave;
-            PageCache<C> pc;
-            page_cache_fill<C>(a, cx, pc, T0);
-            SlicePages<C> sp = slice_pages<C>(a, cx, pc, T0);
-            char* vcur = vlds;
-            char* vnext = vlds + BUF;
-            KBuf<C> kcur, knext;
-            VBuf<C> vb;
-            load_v<C>(a, cx, sp, vb, vcur);
-            load_scales_dma<C>(a, cx, sp, vcur + C::VSTAGE_BYTES);
-            load_k<C>(a, cx, sp, knext);
-            int tile = T0;
-            auto step = [&](auto mask_tag) {
-                constexpr bool M = decltype(mask_tag)::value;
-                full_wait();
-                kcur = knext;
-                sp = slice_pages<C>(a, cx, pc, tile + 1);
-                load_v<C>(a, cx, sp, vb, vnext);
-                load_scales_dma<C>(a, cx, sp, vnext + C::VSTAGE_BYTES);
-                load_k<C>(a, cx, sp, knext);
-                // the whole next stage is issued before this slice computes
-                __builtin_amdgcn_sched_barrier(0);
-                read_scales_lds<C>(cx, vcur + C::VSTAGE_BYTES, kcur);
-                PFrag<C> pf;
-                qk_softmax<C, M>(a, cx, qf, kcur, st, pf, cb);
-                pv<C, M, 0>(cx, vb, pf, st, cb, vcur);
-                char* t = vcur;
-                vcur = vnext;
-                vnext = t;
-                cb += kTileTokens;
-                ++tile;
-            };
-            if constexpr (C::WIN)
-                for (; tile < F0 && tile + 1 < T1;) step(Masked{});
-            for (; tile < F1 && tile + 1 < T1;) step(Full{});
-            if constexpr (C::WIN)
-                for (; tile + 1 < T1;) step(Masked{});
-            full_wait();
-            kcur = knext;
-            read_scales_lds<C>(cx, vcur + C::VSTAGE_BYTES, kcur);
-            PFrag<C> pf;
-            qk_softmax<C, true>(a, cx, qf, kcur, st, pf, cb);
-            pv<C, true, 0>(cx, vb, pf, st, cb, vcur);
-        }
-    } else if (T1 > T0) {
-        int cb = T0 * kTileTokens + 64 * cx.wave;
-        PageCache<C> pc;
-        page_cache_fill<C>(a, cx, pc, T0);
-        SlicePages<C> sp = slice_pages<C>(a, cx, pc, T0);
-        KBuf<C> kb;
-        VBuf<C> vb;
-        load_k<C>(a, cx, sp, kb);
-        int tile = T0;
-        // one tile with a successor: V(tile), QK, K(tile + 1), PV
-        auto step = [&](auto mask_tag) {
-            constexpr bool M = decltype(mask_tag)::value;
-            dma_fence<C>();
-            load_v<C>(a, cx, sp, vb, vlds);
-            PFrag<C> pf;
-            qk_softmax<C, M>(a, cx, qf, kb, st, pf, cb, qlds);
-            sp = slice_pages<C>(a, cx, pc, tile + 1);
-            load_k<C>(a, cx, sp, kb);
-            pv<C, M, C::KVMEM>(cx, vb, pf, st, cb, vlds);
-            cb += kTileTokens;
-            ++tile;
-        };
-        using Masked = BoolTag<true>;
-        using Full = BoolTag<false>;
-        if constexpr (C::WIN)
-            for (; tile < F0 && tile + 1 < T1;) step(Masked{});  // window head
-        for (; tile < F1 && tile + 1 < T1;) step(Full{});        // the bulk
-        if constexpr (C::WIN)
-            for (; tile + 1 < T1;) step(Masked{});               // causal boundary
-        dma_fence<C>();
-        load_v<C>(a, cx, sp, vb, vlds);
-        PFrag<C> pf;
-        qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb, qlds);
-        pv<C, true, 0>(cx, vb, pf, st, cb, vlds);
-    }
+    Range r;
+    r.T0 = part == 0 ? s_min / kTileTokens : max(tb + w0, s_min / kTileTokens);
+    r.T1 = te_task == 0x7FFFFFFF ? ntiles : min(te_task + w0, ntiles);
+    r.F0 = max(r.T0, (s_max + kTileTokens - 1) / kTileTokens);
+    r.F1 = max(r.F0, min(r.T1, e_min / kTileTokens));
+    return r;
+}
 
-    // ---- merge the four waves (fixed order), then store
+template <class C>
+PA_DEV Range task_setup(const TileArgs& a, int idx, Ctx& cx, int& part) {
+    const TaskTiles tt = task_read<C>(a, idx, cx, part);
+    return task_range<C>(a, tt, cx, part);
+}
+
+// Merge the four waves' (m, l, O) of a finished task through LDS in a fixed
+// order and store its rows: directly in bf16 when its (sequence, KV head) has
+// one partition, else as partition `part`'s partial (O times the per-tensor V
+// scale, and the row's max and weight sum). LDS: obuf0 and obuf1 hold
+// ROWS_PAD x OPITCH fp32 each, mlbuf 8 x ROWS_PAD fp32; nothing else is
+// touched. Every wave calls it; wave 0 stores.
+template <class C>
+PA_DEV void finish_task(const TileArgs& a, const Ctx& cx, State<C>& st, int part, float vscale,
+                        float* __restrict__ obuf0, float* __restrict__ obuf1, float* __restrict__ mlbuf) {
+    constexpr int NT = C::NT, D = C::D;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         st.l[nt] += shfl_xor(st.l[nt], 16);
         st.l[nt] += shfl_xor(st.l[nt], 32);
     }
-    __syncthreads();  // V staging tiles are no longer needed
-    float* obuf = reinterpret_cast<float*>(smem);                              // [2][ROWS_PAD][OPITCH]
-    float* mbuf = obuf + 2 * C::ROWS_PAD * C::OPITCH;                          // [4][ROWS_PAD]
-    float* lbuf = mbuf + 4 * C::ROWS_PAD;                                      // [4][ROWS_PAD]
+    lds_barrier();  // every wave's last P*V has read its V tile
+    float* mbuf = mlbuf;                   // [4][ROWS_PAD]
+    float* lbuf = mlbuf + 4 * C::ROWS_PAD;  // [4][ROWS_PAD]
     if (cx.lg == 0) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -1202,7 +1122,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
             lbuf[cx.wave * C::ROWS_PAD + 16 * nt + cx.ln] = st.l[nt];
         }
     }
-    __syncthreads();
+    lds_barrier();
     float Mrow[NT], Lrow[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1223,7 +1143,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
         Lrow[nt] = Lt;
     }
     auto obuf_at = [&](int buf, int nt, int dt) -> float* {
-        return obuf + (buf * C::ROWS_PAD + 16 * nt + cx.ln) * C::OPITCH + 16 * dt + 4 * cx.lg;
+        return (buf ? obuf1 : obuf0) + (16 * nt + cx.ln) * C::OPITCH + 16 * dt + 4 * cx.lg;
     };
     if (cx.wave >= 2) {
 #pragma unroll
@@ -1231,28 +1151,37 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(obuf_at(cx.wave - 2, nt, dt)) = st.o[dt][nt];
     }
-    __syncthreads();
+    lds_barrier();
     if (cx.wave < 2) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] += *reinterpret_cast<f32x4*>(obuf_at(cx.wave, nt, dt));
     }
-    __syncthreads();
+    lds_barrier();
     if (cx.wave == 1) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(obuf_at(0, nt, dt)) = st.o[dt][nt];
     }
-    __syncthreads();
+    lds_barrier();
     if (cx.wave != 0) return;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] += *reinterpret_cast<f32x4*>(obuf_at(0, nt, dt));
 
-    const int nparts = a.plan_free ? (a.uniform_parts > 1 ? a.uniform_parts : 1) : a.seq_parts[2 * cx.b];
+    // partitions of this (sequence, KV head) and its first partial unit
+    const int pair = cx.b * a.num_kv_heads + cx.kvh;
+    int nparts, unit0;
+    if (a.plan_free) {
+        nparts = a.uniform_parts > 1 ? a.uniform_parts : 1;
+        unit0 = pair * nparts;
+    } else {
+        nparts = a.seq_parts[2 * pair];
+        unit0 = a.seq_parts[2 * pair + 1];
+    }
     const int Hq = a.num_kv_heads * a.q_per_kv;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1269,8 +1198,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
                 *reinterpret_cast<u32x2*>(op + 2 * (16 * dt + 4 * cx.lg)) = w;
             }
         } else {
-            const long slot = (a.plan_free ? (long)cx.b * nparts : (long)a.seq_parts[2 * cx.b + 1]) + part;
-            const long prow = (slot * a.num_kv_heads + cx.kvh) * a.rows + r;
+            const long prow = ((long)unit0 + part) * a.rows + r;
             float* po = a.part_o + prow * D;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * cx.lg) = st.o[dt][nt] * vscale;
@@ -1279,6 +1207,270 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
                 a.part_ml[2 * prow + 1] = Lrow[nt];
             }
         }
+    }
+}
+
+// Query fragments of the task in cx by LDS DMA into qbuf: fragment (nt, ks)
+// of lane l at byte 16 ((nt KSTEPS + ks) 64 + l), the layout qk_softmax reads
+// for LDS query instances. Wave w issues fragments w, w + 4, ... Rows past
+// `rows` read row 0 (zeroed where they are read back).
+template <class C>
+PA_DEV void load_q_dma(const TileArgs& a, const Ctx& cx, char* qbuf) {
+    static_assert(C::KV != KV_MXFP4, "bf16 query fragments only");
+    const int Hq = a.num_kv_heads * a.q_per_kv;
+#pragma unroll
+    for (int f = 0; f < C::NT * C::KSTEPS; f += 4) {
+        const int fr = f + cx.wave;
+        if (fr < C::NT * C::KSTEPS) {
+            const int nt = fr / C::KSTEPS, ks = fr % C::KSTEPS;
+            const int r = 16 * nt + cx.ln;
+            const int rr = r < a.rows ? r : 0;
+            const long row = ((long)cx.b * a.qlen + rr / a.q_per_kv) * Hq + (long)cx.kvh * a.q_per_kv + rr % a.q_per_kv;
+            const char* src = reinterpret_cast<const char*>(a.q) + row * C::D * 2 + 2 * kfrag_d0<C>(ks, cx.lg);
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(qbuf + 1024 * fr),
+                                             16, 0, 0);
+        }
+    }
+}
+
+template <class C>
+PA_DEV void read_q_lds(const TileArgs& a, const Ctx& cx, const char* qbuf, QFrag<C>& qf) {
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+        const bool valid = 16 * nt + cx.ln < a.rows;
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(qbuf + 16 * ((nt * C::KSTEPS + ks) * 64 + cx.lane));
+            if (!valid) v = u32x4{0, 0, 0, 0};
+            qf.q[nt][ks] = as_bf16x8(v);
+        }
+    }
+}
+
+// Whole-stage prefetch instances: the workgroup runs its tasks [sb, se) (a
+// list of segments of (sequence, KV head) tile ranges, so that every compute
+// unit streams the same number of tiles). Within a task, stage(tile + 1) --
+// K into the second register set, V and the scales into the other LDS
+// buffer -- is issued right after the wait for stage(tile). The last tile of
+// a task also issues the next task's first stage and its query (by LDS DMA),
+// so the pipeline runs on across the switch; the four-wave merge of the
+// finished task then uses the LDS buffers of the tile just computed.
+template <class C>
+PA_DEV void pf_run(const TileArgs& a, Ctx& cx, int sb, int se, float vscale, char* smem) {
+    constexpr int BUF = C::VSTAGE_BYTES + C::SCALE_BYTES;
+    static_assert(C::ROWS_PAD * C::OPITCH * 4 <= BUF && 8 * C::ROWS_PAD * 4 <= BUF, "merge buffers fit a stage buffer");
+    using Masked = BoolTag<true>;
+    using Full = BoolTag<false>;
+    char* const vlds = smem + cx.wave * C::WAVE_LDS;
+    char* const qbuf = smem + 4 * C::WAVE_LDS;
+    char* vcur = vlds;
+    char* vnext = vlds + BUF;
+    int part = 0, part_n = 0;
+    Range r = task_setup<C>(a, sb, cx, part);
+    Ctx cn = cx;
+    Range rn{0, 0, 0, 0};
+    const bool multi = se - sb > 1;
+    if (multi) rn = task_setup<C>(a, sb + 1, cn, part_n);
+    QFrag<C> qf;
+    load_q<C>(a, cx, qf);
+    PageCache<C> pc, pcn;
+    KBuf<C> kcur, knext;
+    VBuf<C> vb;
+    bool staged = false;  // the current task's first stage is in flight
+    for (int s = sb; s < se; ++s) {
+        const bool has_n = s + 1 < se && rn.T1 > rn.T0;
+        if (r.T1 > r.T0 && !staged) {
+            page_cache_fill<C>(a, cx, pc, r.T0);
+            SlicePages<C> sp = slice_pages<C>(a, cx, pc, r.T0);
+            load_v<C>(a, cx, sp, vb, vcur);
+            load_scales_dma<C>(a, cx, sp, vcur + C::VSTAGE_BYTES);
+            load_k<C>(a, cx, sp, knext);
+        }
+        // the next task's page ids, read while this task streams
+        if (has_n) page_cache_fill<C>(a, cn, pcn, rn.T0);
+        // (initialised here rather than in a helper taking a reference, which
+        // costs the transposed-V instances 30 registers and spills)
+        State<C> st;
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+            st.m[nt] = -__builtin_inff();
+            st.l[nt] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        bool swapped = false;
+        if (r.T1 > r.T0) {
+            int cb = r.T0 * kTileTokens + 64 * cx.wave;
+            int tile = r.T0;
+            auto step = [&](auto mask_tag) {
+                constexpr bool M = decltype(mask_tag)::value;
+                full_wait();
+                kcur = knext;
+                SlicePages<C> sp = slice_pages<C>(a, cx, pc, tile + 1);
+                load_v<C>(a, cx, sp, vb, vnext);
+                load_scales_dma<C>(a, cx, sp, vnext + C::VSTAGE_BYTES);
+                load_k<C>(a, cx, sp, knext);
+                // the whole next stage is issued before this slice computes
+                __builtin_amdgcn_sched_barrier(0);
+                read_scales_lds<C>(cx, vcur + C::VSTAGE_BYTES, kcur);
+                PFrag<C> pf;
+                qk_softmax<C, M>(a, cx, qf, kcur, st, pf, cb);
+                pv<C, M, 0>(cx, vb, pf, st, cb, vcur);
+                char* t = vcur;
+                vcur = vnext;
+                vnext = t;
+                cb += kTileTokens;
+                ++tile;
+            };
+            if constexpr (C::WIN)
+                for (; tile < r.F0 && tile + 1 < r.T1;) step(Masked{});
+            for (; tile < r.F1 && tile + 1 < r.T1;) step(Full{});
+            if constexpr (C::WIN)
+                for (; tile + 1 < r.T1;) step(Masked{});
+            full_wait();
+            kcur = knext;
+            if (has_n) {
+                // the next task's first stage and query go out before this tile computes
+                SlicePages<C> sp = slice_pages<C>(a, cn, pcn, rn.T0);
+                load_v<C>(a, cn, sp, vb, vnext);
+                load_scales_dma<C>(a, cn, sp, vnext + C::VSTAGE_BYTES);
+                load_k<C>(a, cn, sp, knext);
+                load_q_dma<C>(a, cn, qbuf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            read_scales_lds<C>(cx, vcur + C::VSTAGE_BYTES, kcur);
+            PFrag<C> pf;
+            qk_softmax<C, true>(a, cx, qf, kcur, st, pf, cb);
+            pv<C, true, 0>(cx, vb, pf, st, cb, vcur);
+            char* t = vcur;
+            vcur = vnext;
+            vnext = t;
+            swapped = true;
+        }
+        // the merge uses the buffers of the tile just computed (after the swap:
+        // vnext), or with no tiles, the current ones (nothing is in flight there)
+        const int off = (int)((swapped ? vnext : vcur) - vlds);  // the same in every wave
+        finish_task<C>(a, cx, st, part, vscale, reinterpret_cast<float*>(smem + off),
+                       reinterpret_cast<float*>(smem + C::WAVE_LDS + off),
+                       reinterpret_cast<float*>(smem + 2 * C::WAVE_LDS + off));
+        if (s + 1 >= se) break;
+        // switch to the next task
+        staged = has_n;
+        cx = cn;
+        r = rn;
+        part = part_n;
+        pc = pcn;
+        if (staged) {
+            full_wait();  // this wave's share of the query DMA has landed
+            __syncthreads();  // and every other wave's
+            read_q_lds<C>(a, cx, qbuf, qf);
+            __syncthreads();  // before any wave's next query DMA overwrites it
+        } else {
+            load_q<C>(a, cx, qf);
+        }
+        if (s + 2 < se) rn = task_setup<C>(a, s + 2, cn, part_n);
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const TileArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+
+    Ctx cx;
+    cx.lane = threadIdx.x & 63;
+    cx.wave = uniform(threadIdx.x >> 6);
+    cx.ln = cx.lane & 15;
+    cx.lg = cx.lane >> 4;
+    cx.kscale = 1.f;
+    float vscale = 1.f;
+    if constexpr (C::SC == SC_TENSOR) {
+        cx.kscale = *reinterpret_cast<const float*>(a.ks);
+        vscale = *reinterpret_cast<const float*>(a.vs);
+    }
+    if constexpr (C::PF) {
+        // this workgroup's tasks [sb, se)
+        int sb = blockIdx.x, se = blockIdx.x + 1;
+        if (!a.plan_free && a.seg_off) {
+            sb = uniform(a.seg_off[blockIdx.x]);
+            se = uniform(a.seg_off[blockIdx.x + 1]);
+        }
+        if (se > sb) pf_run<C>(a, cx, sb, se, vscale, smem);
+        return;
+    }
+    if constexpr (!C::PF) {
+        int part;
+        const TaskTiles tt = task_read<C>(a, blockIdx.x, cx, part);
+        QFrag<C> qf;
+        load_q<C>(a, cx, qf);
+        State<C> st;
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+            st.m[nt] = -__builtin_inff();
+            st.l[nt] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        char* vlds = smem + cx.wave * C::WAVE_LDS;
+        char* qlds = smem + 4 * C::WAVE_LDS;
+        if constexpr (C::QLDS) {
+            // one copy of the query fragments for the workgroup (the same for every wave)
+            if (cx.wave == 0) {
+#pragma unroll
+                for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+                    for (int ks = 0; ks < C::KSTEPS; ++ks)
+                        *reinterpret_cast<u32x4*>(qlds + 16 * ((nt * C::KSTEPS + ks) * 64 + cx.lane)) =
+                            __builtin_bit_cast(u32x4, qf.q[nt][ks]);
+            }
+            __syncthreads();
+        }
+        const Range rg = task_range<C>(a, tt, cx, part);
+        const int T0 = rg.T0, T1 = rg.T1, F0 = rg.F0, F1 = rg.F1;
+        // Loads run one stage ahead: V(j) is issued at the top of iteration j
+        // (right after PV(j - 1)), K(j + 1) right after QK(j). Every load of a
+        // loop is unconditional and each loop test comes after PV, so the waits
+        // before QK and PV cover exactly the loads of the current slice, never
+        // the prefetch in flight. The last tile runs after the loops with its
+        // own V loads, masked (a no-op on a full tile).
+        if (T1 > T0) {
+            int cb = T0 * kTileTokens + 64 * cx.wave;
+            PageCache<C> pc;
+            page_cache_fill<C>(a, cx, pc, T0);
+            SlicePages<C> sp = slice_pages<C>(a, cx, pc, T0);
+            KBuf<C> kb;
+            VBuf<C> vb;
+            load_k<C>(a, cx, sp, kb);
+            int tile = T0;
+            // one tile with a successor: V(tile), QK, K(tile + 1), PV
+            auto step = [&](auto mask_tag) {
+                constexpr bool M = decltype(mask_tag)::value;
+                dma_fence<C>();
+                load_v<C>(a, cx, sp, vb, vlds);
+                PFrag<C> pf;
+                qk_softmax<C, M>(a, cx, qf, kb, st, pf, cb, qlds);
+                sp = slice_pages<C>(a, cx, pc, tile + 1);
+                load_k<C>(a, cx, sp, kb);
+                pv<C, M, C::KVMEM>(cx, vb, pf, st, cb, vlds);
+                cb += kTileTokens;
+                ++tile;
+            };
+            using Masked = BoolTag<true>;
+            using Full = BoolTag<false>;
+            if constexpr (C::WIN)
+                for (; tile < F0 && tile + 1 < T1;) step(Masked{});  // window head
+            for (; tile < F1 && tile + 1 < T1;) step(Full{});        // the bulk
+            if constexpr (C::WIN)
+                for (; tile + 1 < T1;) step(Masked{});               // causal boundary
+            dma_fence<C>();
+            load_v<C>(a, cx, sp, vb, vlds);
+            PFrag<C> pf;
+            qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb, qlds);
+            pv<C, true, 0>(cx, vb, pf, st, cb, vlds);
+        }
+        // the V staging tiles are free once every wave is past its last P*V
+        float* obuf = reinterpret_cast<float*>(smem);  // [2][ROWS_PAD][OPITCH], then [8][ROWS_PAD]
+        finish_task<C>(a, cx, st, part, vscale, obuf, obuf + C::ROWS_PAD * C::OPITCH,
+                       obuf + 2 * C::ROWS_PAD * C::OPITCH);
     }
 }
 
@@ -1295,8 +1487,8 @@ PA_DEV float wave_sum(float v) {
     return v;
 }
 
-// One wave per output row (b, i, h) of a sequence with more than one
-// partition (at most 64): M = max_p m_p, w_p = 2^(m_p - M),
+// One wave per output row (b, i, h) of a (sequence, KV head) with more than
+// one partition (at most 64): M = max_p m_p, w_p = 2^(m_p - M),
 // out = sum_p w_p O_p / sum_p w_p l_p, summed in partition order (PR #7056,
 // "Bandwidth": the partition reducer). Lane p reads partition p's (m, l); the
 // weighted sum of the O_p rows then runs over p with D/64 elements per lane.
@@ -1312,11 +1504,12 @@ __global__ __launch_bounds__(256) void pa_merge_kernel(const TileArgs a) {
     const int i = rem / Hq, h = rem % Hq;
     const int kvh = h / a.q_per_kv;
     const int r = i * a.q_per_kv + h % a.q_per_kv;
-    const int P = a.plan_free ? a.uniform_parts : a.seq_parts[2 * b];
+    const int pair = b * a.num_kv_heads + kvh;
+    const int P = a.plan_free ? a.uniform_parts : a.seq_parts[2 * pair];
     if (P <= 1) return;
-    const long slot0 = a.plan_free ? (long)b * P : a.seq_parts[2 * b + 1];
-    const long stride = (long)a.num_kv_heads * a.rows;  // rows between consecutive partitions
-    const long prow0 = (slot0 * a.num_kv_heads + kvh) * a.rows + r;
+    const long unit0 = a.plan_free ? (long)pair * P : a.seq_parts[2 * pair + 1];
+    const long stride = a.rows;  // rows between consecutive partitions
+    const long prow0 = unit0 * a.rows + r;
     float m = -__builtin_inff(), l = 0.f;
     if (lane < P) {
         const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * (prow0 + lane * stride));
@@ -1366,6 +1559,7 @@ using TileFn = void (*)(const TileArgs);
 struct Entry {
     KernelKey key;
     TileFn fn;
+    bool segments;  // runs a list of tasks per workgroup (whole-stage prefetch instances)
 };
 
 // Kernel instances are compiled in shards (PA_SHARD 0..3, one object file
@@ -1379,8 +1573,9 @@ struct Entry {
 #define PA_IN_SHARD(n) (PA_SHARD == -1 || PA_SHARD == (n))
 
 #define PA_E(KV, SC, VT, D, PG, NT, QF, W) PA_EM(KV, SC, VT, D, PG, NT, QF, 0, W)
-#define PA_EM(KV, SC, VT, D, PG, NT, QF, MXS, W) \
-    {{KV, SC, VT, D, PG, NT, QF, MXS, W}, &pa_tile_kernel<Cfg<KV, SC, VT, D, PG, NT, QF, MXS, W>>}
+#define PA_EM(KV, SC, VT, D, PG, NT, QF, MXS, W)                      \
+    {{KV, SC, VT, D, PG, NT, QF, MXS, W}, &pa_tile_kernel<Cfg<KV, SC, VT, D, PG, NT, QF, MXS, W>>, \
+     Cfg<KV, SC, VT, D, PG, NT, QF, MXS, W>::PF}
 #define PA_PG(KV, SC, VT, D, NT, W) \
     PA_E(KV, SC, VT, D, 16, NT, 0, W), PA_E(KV, SC, VT, D, 64, NT, 0, W), PA_E(KV, SC, VT, D, 128, NT, 0, W)
 #define PA_NT(KV, SC, VT, D, W) PA_PG(KV, SC, VT, D, 1, W), PA_PG(KV, SC, VT, D, 2, W)
@@ -1414,7 +1609,7 @@ extern const int kShard3Size = sizeof(kShard3) / sizeof(kShard3[0]);
 extern const Entry kShard1[], kShard2[], kShard3[];
 extern const int kShard1Size, kShard2Size, kShard3Size;
 
-static TileFn find(const KernelKey& k) {
+static const Entry* find_entry(const KernelKey& k) {
     const Entry* tables[4] = {kShard0, kShard1, kShard2, kShard3};
     const int sizes[4] = {kShard0Size, kShard1Size, kShard2Size, kShard3Size};
     for (int t = 0; t < 4; ++t)
@@ -1423,9 +1618,19 @@ static TileFn find(const KernelKey& k) {
             if (e.key.kv == k.kv && e.key.scale == k.scale && e.key.vt == k.vt && e.key.head_dim == k.head_dim &&
                 e.key.page == k.page && e.key.ntiles_n == k.ntiles_n && e.key.q_fp8 == k.q_fp8 &&
                 e.key.mx_scaled == k.mx_scaled && e.key.win == k.win)
-                return e.fn;
+                return &e;
         }
     return nullptr;
+}
+
+static TileFn find(const KernelKey& k) {
+    const Entry* e = find_entry(k);
+    return e ? e->fn : nullptr;
+}
+
+bool tile_runs_segments(const KernelKey& key) {
+    const Entry* e = find_entry(key);
+    return e && e->segments;
 }
 
 bool have_tile_kernel(const KernelKey& key) { return find(key) != nullptr; }
