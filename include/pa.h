@@ -369,15 +369,13 @@ size_t pa_plan_workspace_bytes(const pa_plan_t* plan);
 
 /* Plan summary for logging and tests. */
 typedef struct pa_plan_info {
-    int32_t num_tasks;        /* tasks: (sequence, KV head, tile range) records */
+    int32_t num_tasks;        /* workgroups of the tile kernel, one task each */
     int32_t max_parts;        /* largest partition count of any (sequence, KV head) */
     int32_t total_parts;      /* partitions that write partials ((sequence, KV head)s with > 1 partition) */
     int32_t tiles_per_task;   /* target tiles per task the planner chose */
     int32_t merge_needed;     /* 1 if pa_decode launches the merge kernel */
     int32_t num_cus;          /* compute units the plan was sized for */
     int32_t slots;            /* tile workgroups resident at once (compute units x occupancy) */
-    int32_t num_workgroups;   /* workgroups of the tile kernel: num_tasks, or fewer when each runs
-                                 a list of tasks (see pa_plan_host) */
 } pa_plan_info;
 
 pa_status pa_plan_get_info(const pa_plan_t* plan, pa_plan_info* info);
@@ -386,21 +384,16 @@ pa_status pa_plan_get_info(const pa_plan_t* plan, pa_plan_info* info);
  * Host-only planner, for inspection and tests (no device needed): plans as
  * pa_plan would for a device with num_cus compute units holding
  * blocks_per_cu tile workgroups each. Fills
- * tasks_out (int32 x 4 per task: b, kvh | part << 16, tile_begin, tile_end),
- * seq_parts_out (int32 x 2 per (sequence, KV head), b * num_kv_heads + kvh:
- * partitions, first partial unit or -1) and seg_off_out (int32 x
- * (num_workgroups + 1): workgroup w runs tasks [seg_off[w], seg_off[w + 1]) in
- * order). Instances with the whole-stage prefetch (fp8 caches with per-token
- * scales and at most 16 query rows, plain V) take a plan whose workgroups each
- * run a contiguous chunk of the concatenated (sequence, KV head) tile ranges,
- * when that is estimated faster; otherwise there is one task per workgroup,
- * longest first. Capacities are in records; *num_tasks receives the count (when
- * the capacity is too small, nothing is written and PA_ERR_INVALID_ARG returns
- * with *num_tasks set to the required capacity). Any output may be NULL.
+ * tasks_out (int32 x 4 per task, longest first: b, kvh | part << 16,
+ * tile_begin, tile_end) and seq_parts_out (int32 x 2 per (sequence, KV head),
+ * at b * num_kv_heads + kvh: partitions, first partial unit or -1). Capacities
+ * are in records; *num_tasks receives the count (when the capacity is too
+ * small, nothing is written and PA_ERR_INVALID_ARG returns with *num_tasks set
+ * to the required capacity). Any output may be NULL.
  */
 pa_status pa_plan_host(const pa_problem* problem, const int32_t* host_context_lens, int32_t num_cus,
                        int32_t blocks_per_cu, int32_t* tasks_out, int32_t task_capacity, int32_t* num_tasks,
-                       int32_t* seq_parts_out, int32_t* seg_off_out, pa_plan_info* info);
+                       int32_t* seq_parts_out, pa_plan_info* info);
 
 /*
  * Per-kernel timing for measurement. With timing on, pa_decode records HIP

@@ -44,8 +44,7 @@ class pa_problem(ctypes.Structure):
 
 class pa_plan_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "num_tasks", "max_parts", "total_parts", "tiles_per_task", "merge_needed", "num_cus", "slots",
-        "num_workgroups")]
+        "num_tasks", "max_parts", "total_parts", "tiles_per_task", "merge_needed", "num_cus", "slots")]
 
 
 class pa_kv_write_problem(ctypes.Structure):
@@ -92,7 +91,7 @@ def lib() -> ctypes.CDLL:
     L.pa_plan_get_info.restype = ctypes.c_int
     L.pa_plan_get_info.argtypes = [vp, P(pa_plan_info)]
     L.pa_plan_host.restype = ctypes.c_int
-    L.pa_plan_host.argtypes = [P(pa_problem), vp, i32, i32, vp, i32, P(i32), vp, vp, P(pa_plan_info)]
+    L.pa_plan_host.argtypes = [P(pa_problem), vp, i32, i32, vp, i32, P(i32), vp, P(pa_plan_info)]
     L.pa_plan_set_timing.restype = ctypes.c_int
     L.pa_plan_set_timing.argtypes = [vp, i32, i32]
     L.pa_plan_read_timing.restype = ctypes.c_int
@@ -278,25 +277,20 @@ def pa_decode_static(problem: pa_problem, query, key_cache, value_cache, k_scale
     return out
 
 
-def pa_plan_host(problem: pa_problem, host_context_lens=None, num_cus: int = 256, blocks_per_cu: int = 2,
-                 with_offsets: bool = False):
-    """Host-only planner: (tasks int32 [n, 4], pair_parts int32 [B * Hkv, 2], info), plus
-    seg_off int32 [workgroups + 1] when with_offsets."""
+def pa_plan_host(problem: pa_problem, host_context_lens=None, num_cus: int = 256, blocks_per_cu: int = 2):
+    """Host-only planner: (tasks int32 [n, 4], pair_parts int32 [B * Hkv, 2], info)."""
     lens_buf = None if host_context_lens is None else torch.as_tensor(host_context_lens, dtype=torch.int32).contiguous()
     n = ctypes.c_int32()
     info = pa_plan_info()
     lp = None if lens_buf is None else ctypes.c_void_p(lens_buf.data_ptr())
-    _check(lib().pa_plan_host(ctypes.byref(problem), lp, num_cus, blocks_per_cu, None, 0, ctypes.byref(n), None, None,
+    _check(lib().pa_plan_host(ctypes.byref(problem), lp, num_cus, blocks_per_cu, None, 0, ctypes.byref(n), None,
                               ctypes.byref(info)))
     npairs = max(1, problem.num_seqs * problem.num_kv_heads)
     tasks = torch.zeros((max(1, n.value), 4), dtype=torch.int32)
     parts = torch.zeros((npairs, 2), dtype=torch.int32)
-    offs = torch.zeros((info.num_workgroups + 1,), dtype=torch.int32)
     _check(lib().pa_plan_host(ctypes.byref(problem), lp, num_cus, blocks_per_cu, ctypes.c_void_p(tasks.data_ptr()),
-                              n.value, ctypes.byref(n), ctypes.c_void_p(parts.data_ptr()),
-                              ctypes.c_void_p(offs.data_ptr()), ctypes.byref(info)))
-    out = (tasks[:n.value], parts[:problem.num_seqs * problem.num_kv_heads], info)
-    return out + (offs,) if with_offsets else out
+                              n.value, ctypes.byref(n), ctypes.c_void_p(parts.data_ptr()), ctypes.byref(info)))
+    return tasks[:n.value], parts[:problem.num_seqs * problem.num_kv_heads], info
 
 
 def device_tensors(case, device="cuda"):

@@ -10,7 +10,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -149,8 +148,7 @@ pa::KernelKey key_of(const pa_problem& p) {
 }
 
 struct Plan {
-    std::vector<int32_t> tasks;      // 4 per task, in workgroup order
-    std::vector<int32_t> seg_off;    // workgroup w runs tasks [seg_off[w], seg_off[w + 1]); empty: task w
+    std::vector<int32_t> tasks;      // 4 per task, one task per workgroup
     std::vector<int32_t> seq_parts;  // 2 per (sequence, KV head): partitions, first partial unit or -1
     pa_plan_info info{};
 };
@@ -230,8 +228,7 @@ static double tile_bytes_of(const pa_problem& p) {
 }
 
 // Cut every (sequence, KV head) into partitions of contiguous tiles.
-pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int blocks_per_cu, bool segments_ok,
-                     Plan* out) {
+pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int blocks_per_cu, Plan* out) {
     const int B = p.num_seqs, H = p.num_kv_heads;
     const int max_parts = p.max_partitions > 0 ? p.max_partitions : 64;
     const int slots = std::max(1, num_cus * std::max(1, blocks_per_cu));
@@ -292,89 +289,10 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int 
             }
         }
     }
-    // Segment plan (instances that run a task list per workgroup): the
-    // (sequence, KV head) tile ranges, concatenated, cut into one contiguous
-    // chunk per resident workgroup slot, so every compute unit streams the same
-    // number of tiles (to one tile); a chunk may hold the end of one range and
-    // the start of the next, whose first stage the workgroup prefetches while
-    // it finishes the first. Taken whenever there are fewer (sequence, KV
-    // head) pairs than slots, where the per-task plan has to split ranges
-    // anyway and can only balance them to a tile per task.
-    const long total = work;
-    int W = (int)std::min<long>(slots, std::max<long>(1, total));
-    const bool use_segments = segments_ok && p.task_budget == 0 && p.max_partitions == 0 && B > 0 &&
-                              (long)B * H < slots && total >= W;
     out->tasks.clear();
-    out->seg_off.clear();
     out->seq_parts.assign(2 * (size_t)B * H, 0);
     int units = 0, maxp = 0;
-    if (use_segments) {
-        std::vector<int> pair_parts((size_t)B * H, 0);
-        // Greedy chunks of at most T tiles, where every range beyond a
-        // chunk's first counts one tile more (a switch costs about a tile's
-        // time: the four waves meet for the merge, the slowest last); T is the
-        // smallest that fits in W workgroups.
-        auto chunk_plan = [&](long T, std::vector<std::array<long, 4>>* segs, std::vector<int>* off) -> long {
-            long wgs = 0, pos = 0, pstart = 0;
-            int pb = 0;  // pair index (b * H + kvh) holding `pos`
-            const long npairs = (long)B * H;
-            if (segs) segs->clear();
-            if (off) off->assign(1, 0);
-            while (true) {
-                while (pb < npairs && pos >= pstart + tiles[pb / H]) pstart += tiles[pb++ / H];
-                if (pb >= npairs) break;
-                long budget = T;
-                ++wgs;
-                while (pb < npairs && budget > 0) {
-                    const long avail = pstart + tiles[pb / H] - pos;
-                    const long take = std::min(avail, budget);
-                    if (segs) segs->push_back({pb, pos - pstart, pos - pstart + take, 0});
-                    pos += take;
-                    budget -= take + 1;  // the next range costs a switch
-                    if (take == avail) {
-                        pstart += tiles[pb / H];
-                        ++pb;
-                        while (pb < npairs && tiles[pb / H] == 0) ++pb;
-                    }
-                }
-                if (off) off->push_back(segs ? (int)segs->size() : 0);
-            }
-            return wgs;
-        };
-        long lo = std::max<long>(1, (total + W - 1) / W), hi = lo;
-        while (chunk_plan(hi, nullptr, nullptr) > W) hi *= 2;
-        while (lo < hi) {
-            const long mid = (lo + hi) / 2;
-            if (chunk_plan(mid, nullptr, nullptr) <= W) hi = mid; else lo = mid + 1;
-        }
-        std::vector<std::array<long, 4>> segs;
-        std::vector<int> off;
-        chunk_plan(lo, &segs, &off);
-        for (const auto& sg : segs) {
-            const int bb = (int)(sg[0] / H), h = (int)(sg[0] % H);
-            out->tasks.insert(out->tasks.end(), {bb, h | (pair_parts[sg[0]] << 16), first[bb] + (int)sg[1],
-                                                 first[bb] + (int)sg[2]});
-            pair_parts[sg[0]]++;
-        }
-        out->seg_off.assign(off.begin(), off.end());
-        W = (int)off.size() - 1;
-        // pairs with no tiles still get one (empty) task: their rows are written as zeros
-        for (int bb = 0; bb < B; ++bb)
-            for (int h = 0; h < H; ++h)
-                if (pair_parts[(size_t)bb * H + h] == 0) {
-                    out->tasks.insert(out->tasks.end(), {bb, h, first[bb], first[bb]});
-                    pair_parts[(size_t)bb * H + h] = 1;
-                    out->seg_off.back() = (int32_t)(out->tasks.size() / 4);
-                }
-        for (size_t pr = 0; pr < pair_parts.size(); ++pr) {
-            const int P = pair_parts[pr];
-            maxp = std::max(maxp, P);
-            out->seq_parts[2 * pr] = P;
-            out->seq_parts[2 * pr + 1] = P > 1 ? units : -1;
-            if (P > 1) units += P;
-        }
-        tpt = (int)lo;
-    } else {
+    {
         for (int b = 0; b < B; ++b) {
             const int P = parts[b];
             maxp = std::max(maxp, P);
@@ -404,7 +322,6 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int 
     const size_t n = out->tasks.size() / 4;
     if (n > 0x7FFFFFFF / 4) return fail(PA_ERR_UNSUPPORTED, "too many tasks");
     out->info.num_tasks = (int32_t)n;
-    out->info.num_workgroups = use_segments ? W : (int32_t)n;
     out->info.max_parts = maxp;
     out->info.total_parts = units;
     out->info.tiles_per_task = tpt;
@@ -422,7 +339,6 @@ struct pa_plan {
     pa_plan_info info{};
     int device = -1;
     int32_t* d_tasks = nullptr;
-    int32_t* d_seg_off = nullptr;  // null: one task per workgroup
     int32_t* d_seq_parts = nullptr;
     float* d_part_ml = nullptr;
     float* d_part_o = nullptr;
@@ -442,13 +358,12 @@ const char* pa_version(void) { return "pa_decode gfx950 0.1"; }
 
 pa_status pa_plan_host(const pa_problem* problem, const int32_t* host_context_lens, int32_t num_cus,
                        int32_t blocks_per_cu, int32_t* tasks_out, int32_t task_capacity, int32_t* num_tasks,
-                       int32_t* seq_parts_out, int32_t* seg_off_out, pa_plan_info* info) {
+                       int32_t* seq_parts_out, pa_plan_info* info) {
     pa_status st = validate(problem);
     if (st != PA_OK) return st;
     if (num_cus < 1 || blocks_per_cu < 1) return fail(PA_ERR_INVALID_ARG, "num_cus and blocks_per_cu must be >= 1");
     Plan plan;
-    st = build_plan(*problem, host_context_lens, num_cus, blocks_per_cu, pa::tile_runs_segments(key_of(*problem)),
-                    &plan);
+    st = build_plan(*problem, host_context_lens, num_cus, blocks_per_cu, &plan);
     if (st != PA_OK) return st;
     if (num_tasks) *num_tasks = plan.info.num_tasks;
     if (info) *info = plan.info;
@@ -457,12 +372,6 @@ pa_status pa_plan_host(const pa_problem* problem, const int32_t* host_context_le
         std::memcpy(tasks_out, plan.tasks.data(), plan.tasks.size() * sizeof(int32_t));
     }
     if (seq_parts_out) std::memcpy(seq_parts_out, plan.seq_parts.data(), plan.seq_parts.size() * sizeof(int32_t));
-    if (seg_off_out) {
-        if (plan.seg_off.empty())
-            for (int32_t w = 0; w <= plan.info.num_workgroups; ++w) seg_off_out[w] = w;
-        else
-            std::memcpy(seg_off_out, plan.seg_off.data(), plan.seg_off.size() * sizeof(int32_t));
-    }
     return PA_OK;
 }
 
@@ -479,8 +388,7 @@ pa_status pa_plan(const pa_problem* problem, const int32_t* host_context_lens, p
     const pa::KernelKey key = key_of(*problem);
     if (!pa::have_tile_kernel(key)) return fail(PA_ERR_UNSUPPORTED, "no kernel instance for this problem");
     Plan plan;
-    st = build_plan(*problem, host_context_lens, dev.num_cus, pa::tile_blocks_per_cu(key), pa::tile_runs_segments(key),
-                    &plan);
+    st = build_plan(*problem, host_context_lens, dev.num_cus, pa::tile_blocks_per_cu(key), &plan);
     if (st != PA_OK) return st;
 
     pa_plan_t* p = new (std::nothrow) pa_plan_t();
@@ -501,27 +409,13 @@ pa_status pa_plan(const pa_problem* problem, const int32_t* host_context_lens, p
         pa_plan_destroy(p);
         return fail(PA_ERR_OOM, "workspace allocation failed: %s", hipGetErrorString(e));
     }
-    size_t seg_b = 0;
-    if (!plan.seg_off.empty()) {
-        seg_b = plan.seg_off.size() * sizeof(int32_t);
-        if ((e = hipMalloc(&p->d_seg_off, seg_b)) != hipSuccess) {
-            pa_plan_destroy(p);
-            return fail(PA_ERR_OOM, "workspace allocation failed: %s", hipGetErrorString(e));
-        }
-    }
-    p->ws_bytes = tasks_b + seg_b + seq_b + ml_b + o_b;
+    p->ws_bytes = tasks_b + seq_b + ml_b + o_b;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (!plan.tasks.empty() &&
         (e = hipMemcpyAsync(p->d_tasks, plan.tasks.data(), plan.tasks.size() * sizeof(int32_t), hipMemcpyHostToDevice, s)) !=
             hipSuccess) {
         pa_plan_destroy(p);
         return fail(PA_ERR_HIP, "task upload failed: %s", hipGetErrorString(e));
-    }
-    if (!plan.seg_off.empty() &&
-        (e = hipMemcpyAsync(p->d_seg_off, plan.seg_off.data(), plan.seg_off.size() * sizeof(int32_t),
-                            hipMemcpyHostToDevice, s)) != hipSuccess) {
-        pa_plan_destroy(p);
-        return fail(PA_ERR_HIP, "task offsets upload failed: %s", hipGetErrorString(e));
     }
     if (!plan.seq_parts.empty() &&
         (e = hipMemcpyAsync(p->d_seq_parts, plan.seq_parts.data(), plan.seq_parts.size() * sizeof(int32_t),
@@ -535,19 +429,17 @@ pa_status pa_plan(const pa_problem* problem, const int32_t* host_context_lens, p
         return fail(PA_ERR_HIP, "plan upload sync failed: %s", hipGetErrorString(e));
     }
     if (std::getenv("PA_LOG"))
-        std::fprintf(stderr, "[pa] plan: %d tasks in %d workgroups on %d slots, %d tiles/task target, max %d partitions, %d partial units, %zu B workspace\n",
-                     plan.info.num_tasks, plan.info.num_workgroups, plan.info.slots, plan.info.tiles_per_task,
-                     plan.info.max_parts, plan.info.total_parts, p->ws_bytes);
+        std::fprintf(stderr, "[pa] plan: %d tasks on %d slots, %d tiles/task target, max %d partitions, %d partial units, %zu B workspace\n",
+                     plan.info.num_tasks, plan.info.slots, plan.info.tiles_per_task, plan.info.max_parts,
+                     plan.info.total_parts, p->ws_bytes);
     *plan_out = p;
     return PA_OK;
 }
 
 void pa_plan_destroy(pa_plan_t* p) {
     if (!p) return;
-    if (p->d_tasks || p->d_seg_off || p->d_seq_parts || p->d_part_ml || p->d_part_o || !p->ev.empty())
-        (void)hipDeviceSynchronize();
+    if (p->d_tasks || p->d_seq_parts || p->d_part_ml || p->d_part_o || !p->ev.empty()) (void)hipDeviceSynchronize();
     if (p->d_tasks) (void)hipFree(p->d_tasks);
-    if (p->d_seg_off) (void)hipFree(p->d_seg_off);
     if (p->d_seq_parts) (void)hipFree(p->d_seq_parts);
     if (p->d_part_ml) (void)hipFree(p->d_part_ml);
     if (p->d_part_o) (void)hipFree(p->d_part_o);
@@ -604,7 +496,6 @@ pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_ca
     a.context_lens = context_lens;
     a.out = out;
     a.tasks = plan->d_tasks;
-    a.seg_off = plan->d_seg_off;
     a.seq_parts = plan->d_seq_parts;
     a.part_ml = plan->d_part_ml;
     a.part_o = plan->d_part_o;
@@ -626,7 +517,7 @@ pa_status pa_decode(const pa_plan_t* plan, const void* query, const void* key_ca
     const bool rec = mp->timing && mp->ncalls < mp->max_calls;
     hipEvent_t* ev = rec ? &mp->ev[3 * (size_t)mp->ncalls] : nullptr;
     if (rec && (e = hipEventRecord(ev[0], s)) != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    e = pa::launch_tile(plan->key, a, plan->info.num_workgroups, s);
+    e = pa::launch_tile(plan->key, a, plan->info.num_tasks, s);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "tile kernel launch failed: %s", hipGetErrorString(e));
     if (rec && (e = hipEventRecord(ev[1], s)) != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
     if (plan->info.merge_needed) {

@@ -26,8 +26,7 @@ struct TileArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     void* out;                 // bf16 [B][qlen][Hq][D]
-    const int32_t* tasks;      // int32 x 4 per task, in workgroup order
-    const int32_t* seg_off;    // tasks [seg_off[w], seg_off[w + 1]) of workgroup w, or null: task w
+    const int32_t* tasks;      // int32 x 4 per task, one per workgroup
     const int32_t* seq_parts;  // int32 x 2 per (sequence, KV head): partitions, first partial unit
     float* part_ml;            // [units][rows][2]: running max (base 2), sum of weights
     float* part_o;             // [units][rows][D]: weighted sum of V (times the per-tensor V scale)
@@ -97,9 +96,6 @@ hipError_t launch_merge(const TileArgs& args, int head_dim, hipStream_t stream);
 
 // Whether an instance exists for `key`.
 bool have_tile_kernel(const KernelKey& key);
-
-// Whether the instance for `key` runs a list of tasks per workgroup (seg_off).
-bool tile_runs_segments(const KernelKey& key);
 
 // Tile-kernel workgroups of `key` that fit on one compute unit at once.
 int tile_blocks_per_cu(const KernelKey& key);

@@ -256,9 +256,7 @@ struct Cfg {
     static constexpr int VSTAGE_BYTES = VDMA ? 64 * ROWB : (STAGE_V ? 32 * VPITCH : 0);  // per wave
     static constexpr int SCALE_BYTES = PF ? 512 : 0;                 // K then V scales of 64 tokens (fp32)
     static constexpr int WAVE_LDS = (PF ? 2 : 1) * (VSTAGE_BYTES + SCALE_BYTES);  // per wave
-    // query fragments in LDS: one copy per workgroup (QLDS), or the next task's
-    // query, brought by LDS DMA while the current task streams (PF)
-    static constexpr int QLDS_BYTES = (QLDS || PF) ? NT * KSTEPS * 64 * 16 : 0;
+    static constexpr int QLDS_BYTES = QLDS ? NT * KSTEPS * 64 * 16 : 0;
     static constexpr int ROWS_PAD = 16 * NT;
     static constexpr int OPITCH = D + 4;                             // floats
     static constexpr int EPI_BYTES = 2 * ROWS_PAD * OPITCH * 4 + 2 * 4 * ROWS_PAD * 4;
@@ -422,16 +420,26 @@ PA_DEV void load_q(const TileArgs& a, const Ctx& cx, QFrag<C>& qf) {
     }
 }
 
-// Page id of table slot `slot` (pinned to block 0 past the owned pages and
-// before the first column any row reads, and clamped into the pool).
-template <bool MASK>
+// Page id of table slot `slot` (pinned to block 0 past the owned pages and,
+// with causal rows or a window, before the first column any row reads;
+// clamped into the pool).
+template <class C, bool MASK>
 PA_DEV int page_of(const TileArgs& a, const Ctx& cx, int slot) {
     // The read is unconditional, since a per-lane branch here would make every
     // loop that refills page ids divergent. Outside the read columns it
-    // re-reads the nearest one, and the select pins the slot to block 0.
-    const int col = MASK ? min(max(slot, cx.pg_first), max(cx.npages - 1, 0)) : slot;
-    int p = cx.bt_row[col];
-    if (MASK && (slot >= cx.npages || slot < cx.pg_first)) p = 0;
+    // re-reads the nearest one, and the select pins the slot to block 0. The
+    // in-range test is one comparison: with two, the compiler skips the load
+    // for the lanes the select discards, which is such a branch.
+    int p;
+    if constexpr (C::WIN) {
+        const int col = MASK ? min(max(slot, cx.pg_first), max(cx.npages - 1, 0)) : slot;
+        p = cx.bt_row[col];
+        if (MASK && (unsigned)(slot - cx.pg_first) >= (unsigned)(cx.npages - cx.pg_first)) p = 0;
+    } else {
+        const int col = MASK ? min(slot, max(cx.npages - 1, 0)) : slot;
+        p = cx.bt_row[col];
+        if (MASK && slot >= cx.npages) p = 0;
+    }
     p = p < 0 ? 0 : (p >= a.num_blocks ? a.num_blocks - 1 : p);
     return p;
 }
@@ -496,7 +504,7 @@ PA_DEV void page_cache_fill(const TileArgs& a, const Ctx& cx, PageCache<C>& pc, 
     pc.tile0 = tile0;
     const int tile = tile0 + cx.lane / C::NPC;
     const int slot = (tile * kTileTokens + 64 * cx.wave) / C::PG + cx.lane % C::NPC;
-    pc.pgv = page_of<true>(a, cx, slot);
+    pc.pgv = page_of<C, true>(a, cx, slot);
 }
 
 PA_DEV int lane_value(int v, int src_lane) { return __builtin_amdgcn_ds_bpermute(src_lane << 2, v); }
@@ -1210,103 +1218,75 @@ PA_DEV void finish_task(const TileArgs& a, const Ctx& cx, State<C>& st, int part
     }
 }
 
-// Query fragments of the task in cx by LDS DMA into qbuf: fragment (nt, ks)
-// of lane l at byte 16 ((nt KSTEPS + ks) 64 + l), the layout qk_softmax reads
-// for LDS query instances. Wave w issues fragments w, w + 4, ... Rows past
-// `rows` read row 0 (zeroed where they are read back).
 template <class C>
-PA_DEV void load_q_dma(const TileArgs& a, const Ctx& cx, char* qbuf) {
-    static_assert(C::KV != KV_MXFP4, "bf16 query fragments only");
-    const int Hq = a.num_kv_heads * a.q_per_kv;
-#pragma unroll
-    for (int f = 0; f < C::NT * C::KSTEPS; f += 4) {
-        const int fr = f + cx.wave;
-        if (fr < C::NT * C::KSTEPS) {
-            const int nt = fr / C::KSTEPS, ks = fr % C::KSTEPS;
-            const int r = 16 * nt + cx.ln;
-            const int rr = r < a.rows ? r : 0;
-            const long row = ((long)cx.b * a.qlen + rr / a.q_per_kv) * Hq + (long)cx.kvh * a.q_per_kv + rr % a.q_per_kv;
-            const char* src = reinterpret_cast<const char*>(a.q) + row * C::D * 2 + 2 * kfrag_d0<C>(ks, cx.lg);
-            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(qbuf + 1024 * fr),
-                                             16, 0, 0);
-        }
-    }
-}
+__global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const TileArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
 
-template <class C>
-PA_DEV void read_q_lds(const TileArgs& a, const Ctx& cx, const char* qbuf, QFrag<C>& qf) {
-#pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
-        const bool valid = 16 * nt + cx.ln < a.rows;
-#pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            u32x4 v = *reinterpret_cast<const u32x4*>(qbuf + 16 * ((nt * C::KSTEPS + ks) * 64 + cx.lane));
-            if (!valid) v = u32x4{0, 0, 0, 0};
-            qf.q[nt][ks] = as_bf16x8(v);
-        }
+    Ctx cx;
+    cx.lane = threadIdx.x & 63;
+    cx.wave = uniform(threadIdx.x >> 6);
+    cx.ln = cx.lane & 15;
+    cx.lg = cx.lane >> 4;
+    int part;
+    const TaskTiles tt = task_read<C>(a, blockIdx.x, cx, part);
+    cx.kscale = 1.f;
+    float vscale = 1.f;
+    if constexpr (C::SC == SC_TENSOR) {
+        cx.kscale = *reinterpret_cast<const float*>(a.ks);
+        vscale = *reinterpret_cast<const float*>(a.vs);
     }
-}
-
-// Whole-stage prefetch instances: the workgroup runs its tasks [sb, se) (a
-// list of segments of (sequence, KV head) tile ranges, so that every compute
-// unit streams the same number of tiles). Within a task, stage(tile + 1) --
-// K into the second register set, V and the scales into the other LDS
-// buffer -- is issued right after the wait for stage(tile). The last tile of
-// a task also issues the next task's first stage and its query (by LDS DMA),
-// so the pipeline runs on across the switch; the four-wave merge of the
-// finished task then uses the LDS buffers of the tile just computed.
-template <class C>
-PA_DEV void pf_run(const TileArgs& a, Ctx& cx, int sb, int se, float vscale, char* smem) {
-    constexpr int BUF = C::VSTAGE_BYTES + C::SCALE_BYTES;
-    static_assert(C::ROWS_PAD * C::OPITCH * 4 <= BUF && 8 * C::ROWS_PAD * 4 <= BUF, "merge buffers fit a stage buffer");
-    using Masked = BoolTag<true>;
-    using Full = BoolTag<false>;
-    char* const vlds = smem + cx.wave * C::WAVE_LDS;
-    char* const qbuf = smem + 4 * C::WAVE_LDS;
-    char* vcur = vlds;
-    char* vnext = vlds + BUF;
-    int part = 0, part_n = 0;
-    Range r = task_setup<C>(a, sb, cx, part);
-    Ctx cn = cx;
-    Range rn{0, 0, 0, 0};
-    const bool multi = se - sb > 1;
-    if (multi) rn = task_setup<C>(a, sb + 1, cn, part_n);
     QFrag<C> qf;
     load_q<C>(a, cx, qf);
-    PageCache<C> pc, pcn;
-    KBuf<C> kcur, knext;
-    VBuf<C> vb;
-    bool staged = false;  // the current task's first stage is in flight
-    for (int s = sb; s < se; ++s) {
-        const bool has_n = s + 1 < se && rn.T1 > rn.T0;
-        if (r.T1 > r.T0 && !staged) {
-            page_cache_fill<C>(a, cx, pc, r.T0);
-            SlicePages<C> sp = slice_pages<C>(a, cx, pc, r.T0);
+    // (initialised here rather than in a helper taking a reference, which
+    // costs the transposed-V instances 30 registers and spills)
+    State<C> st;
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+        st.m[nt] = -__builtin_inff();
+        st.l[nt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    char* vlds = smem + cx.wave * C::WAVE_LDS;
+    char* qlds = smem + 4 * C::WAVE_LDS;
+    if constexpr (C::QLDS) {
+        // one copy of the query fragments for the workgroup (the same for every wave)
+        if (cx.wave == 0) {
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+                for (int ks = 0; ks < C::KSTEPS; ++ks)
+                    *reinterpret_cast<u32x4*>(qlds + 16 * ((nt * C::KSTEPS + ks) * 64 + cx.lane)) =
+                        __builtin_bit_cast(u32x4, qf.q[nt][ks]);
+        }
+        __syncthreads();
+    }
+    const Range rg = task_range<C>(a, tt, cx, part);
+    const int T0 = rg.T0, T1 = rg.T1, F0 = rg.F0, F1 = rg.F1;
+    using Masked = BoolTag<true>;
+    using Full = BoolTag<false>;
+    if constexpr (C::PF) {
+        if (T1 > T0) {
+            // stage = K (registers), V tile and scale block (LDS) of one slice;
+            // stage(tile + 1) is issued right after the wait for stage(tile)
+            constexpr int BUF = C::VSTAGE_BYTES + C::SCALE_BYTES;
+            int cb = T0 * kTileTokens + 64 * cx.wave;
+            PageCache<C> pc;
+            page_cache_fill<C>(a, cx, pc, T0);
+            SlicePages<C> sp = slice_pages<C>(a, cx, pc, T0);
+            char* vcur = vlds;
+            char* vnext = vlds + BUF;
+            KBuf<C> kcur, knext;
+            VBuf<C> vb;
             load_v<C>(a, cx, sp, vb, vcur);
             load_scales_dma<C>(a, cx, sp, vcur + C::VSTAGE_BYTES);
             load_k<C>(a, cx, sp, knext);
-        }
-        // the next task's page ids, read while this task streams
-        if (has_n) page_cache_fill<C>(a, cn, pcn, rn.T0);
-        // (initialised here rather than in a helper taking a reference, which
-        // costs the transposed-V instances 30 registers and spills)
-        State<C> st;
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) {
-            st.m[nt] = -__builtin_inff();
-            st.l[nt] = 0.f;
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        bool swapped = false;
-        if (r.T1 > r.T0) {
-            int cb = r.T0 * kTileTokens + 64 * cx.wave;
-            int tile = r.T0;
+            int tile = T0;
             auto step = [&](auto mask_tag) {
                 constexpr bool M = decltype(mask_tag)::value;
                 full_wait();
                 kcur = knext;
-                SlicePages<C> sp = slice_pages<C>(a, cx, pc, tile + 1);
+                sp = slice_pages<C>(a, cx, pc, tile + 1);
                 load_v<C>(a, cx, sp, vb, vnext);
                 load_scales_dma<C>(a, cx, sp, vnext + C::VSTAGE_BYTES);
                 load_k<C>(a, cx, sp, knext);
@@ -1323,155 +1303,60 @@ PA_DEV void pf_run(const TileArgs& a, Ctx& cx, int sb, int se, float vscale, cha
                 ++tile;
             };
             if constexpr (C::WIN)
-                for (; tile < r.F0 && tile + 1 < r.T1;) step(Masked{});
-            for (; tile < r.F1 && tile + 1 < r.T1;) step(Full{});
+                for (; tile < F0 && tile + 1 < T1;) step(Masked{});
+            for (; tile < F1 && tile + 1 < T1;) step(Full{});
             if constexpr (C::WIN)
-                for (; tile + 1 < r.T1;) step(Masked{});
+                for (; tile + 1 < T1;) step(Masked{});
             full_wait();
             kcur = knext;
-            if (has_n) {
-                // the next task's first stage and query go out before this tile computes
-                SlicePages<C> sp = slice_pages<C>(a, cn, pcn, rn.T0);
-                load_v<C>(a, cn, sp, vb, vnext);
-                load_scales_dma<C>(a, cn, sp, vnext + C::VSTAGE_BYTES);
-                load_k<C>(a, cn, sp, knext);
-                load_q_dma<C>(a, cn, qbuf);
-                __builtin_amdgcn_sched_barrier(0);
-            }
             read_scales_lds<C>(cx, vcur + C::VSTAGE_BYTES, kcur);
             PFrag<C> pf;
             qk_softmax<C, true>(a, cx, qf, kcur, st, pf, cb);
             pv<C, true, 0>(cx, vb, pf, st, cb, vcur);
-            char* t = vcur;
-            vcur = vnext;
-            vnext = t;
-            swapped = true;
         }
-        // the merge uses the buffers of the tile just computed (after the swap:
-        // vnext), or with no tiles, the current ones (nothing is in flight there)
-        const int off = (int)((swapped ? vnext : vcur) - vlds);  // the same in every wave
-        finish_task<C>(a, cx, st, part, vscale, reinterpret_cast<float*>(smem + off),
-                       reinterpret_cast<float*>(smem + C::WAVE_LDS + off),
-                       reinterpret_cast<float*>(smem + 2 * C::WAVE_LDS + off));
-        if (s + 1 >= se) break;
-        // switch to the next task
-        staged = has_n;
-        cx = cn;
-        r = rn;
-        part = part_n;
-        pc = pcn;
-        if (staged) {
-            full_wait();  // this wave's share of the query DMA has landed
-            __syncthreads();  // and every other wave's
-            read_q_lds<C>(a, cx, qbuf, qf);
-            __syncthreads();  // before any wave's next query DMA overwrites it
-        } else {
-            load_q<C>(a, cx, qf);
-        }
-        if (s + 2 < se) rn = task_setup<C>(a, s + 2, cn, part_n);
-    }
-}
-
-template <class C>
-__global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const TileArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-
-    Ctx cx;
-    cx.lane = threadIdx.x & 63;
-    cx.wave = uniform(threadIdx.x >> 6);
-    cx.ln = cx.lane & 15;
-    cx.lg = cx.lane >> 4;
-    cx.kscale = 1.f;
-    float vscale = 1.f;
-    if constexpr (C::SC == SC_TENSOR) {
-        cx.kscale = *reinterpret_cast<const float*>(a.ks);
-        vscale = *reinterpret_cast<const float*>(a.vs);
-    }
-    if constexpr (C::PF) {
-        // this workgroup's tasks [sb, se)
-        int sb = blockIdx.x, se = blockIdx.x + 1;
-        if (!a.plan_free && a.seg_off) {
-            sb = uniform(a.seg_off[blockIdx.x]);
-            se = uniform(a.seg_off[blockIdx.x + 1]);
-        }
-        if (se > sb) pf_run<C>(a, cx, sb, se, vscale, smem);
-        return;
-    }
-    if constexpr (!C::PF) {
-        int part;
-        const TaskTiles tt = task_read<C>(a, blockIdx.x, cx, part);
-        QFrag<C> qf;
-        load_q<C>(a, cx, qf);
-        State<C> st;
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) {
-            st.m[nt] = -__builtin_inff();
-            st.l[nt] = 0.f;
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        char* vlds = smem + cx.wave * C::WAVE_LDS;
-        char* qlds = smem + 4 * C::WAVE_LDS;
-        if constexpr (C::QLDS) {
-            // one copy of the query fragments for the workgroup (the same for every wave)
-            if (cx.wave == 0) {
-#pragma unroll
-                for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-                    for (int ks = 0; ks < C::KSTEPS; ++ks)
-                        *reinterpret_cast<u32x4*>(qlds + 16 * ((nt * C::KSTEPS + ks) * 64 + cx.lane)) =
-                            __builtin_bit_cast(u32x4, qf.q[nt][ks]);
-            }
-            __syncthreads();
-        }
-        const Range rg = task_range<C>(a, tt, cx, part);
-        const int T0 = rg.T0, T1 = rg.T1, F0 = rg.F0, F1 = rg.F1;
+    } else if (T1 > T0) {
         // Loads run one stage ahead: V(j) is issued at the top of iteration j
         // (right after PV(j - 1)), K(j + 1) right after QK(j). Every load of a
         // loop is unconditional and each loop test comes after PV, so the waits
         // before QK and PV cover exactly the loads of the current slice, never
         // the prefetch in flight. The last tile runs after the loops with its
         // own V loads, masked (a no-op on a full tile).
-        if (T1 > T0) {
-            int cb = T0 * kTileTokens + 64 * cx.wave;
-            PageCache<C> pc;
-            page_cache_fill<C>(a, cx, pc, T0);
-            SlicePages<C> sp = slice_pages<C>(a, cx, pc, T0);
-            KBuf<C> kb;
-            VBuf<C> vb;
-            load_k<C>(a, cx, sp, kb);
-            int tile = T0;
-            // one tile with a successor: V(tile), QK, K(tile + 1), PV
-            auto step = [&](auto mask_tag) {
-                constexpr bool M = decltype(mask_tag)::value;
-                dma_fence<C>();
-                load_v<C>(a, cx, sp, vb, vlds);
-                PFrag<C> pf;
-                qk_softmax<C, M>(a, cx, qf, kb, st, pf, cb, qlds);
-                sp = slice_pages<C>(a, cx, pc, tile + 1);
-                load_k<C>(a, cx, sp, kb);
-                pv<C, M, C::KVMEM>(cx, vb, pf, st, cb, vlds);
-                cb += kTileTokens;
-                ++tile;
-            };
-            using Masked = BoolTag<true>;
-            using Full = BoolTag<false>;
-            if constexpr (C::WIN)
-                for (; tile < F0 && tile + 1 < T1;) step(Masked{});  // window head
-            for (; tile < F1 && tile + 1 < T1;) step(Full{});        // the bulk
-            if constexpr (C::WIN)
-                for (; tile + 1 < T1;) step(Masked{});               // causal boundary
+        int cb = T0 * kTileTokens + 64 * cx.wave;
+        PageCache<C> pc;
+        page_cache_fill<C>(a, cx, pc, T0);
+        SlicePages<C> sp = slice_pages<C>(a, cx, pc, T0);
+        KBuf<C> kb;
+        VBuf<C> vb;
+        load_k<C>(a, cx, sp, kb);
+        int tile = T0;
+        // one tile with a successor: V(tile), QK, K(tile + 1), PV
+        auto step = [&](auto mask_tag) {
+            constexpr bool M = decltype(mask_tag)::value;
             dma_fence<C>();
             load_v<C>(a, cx, sp, vb, vlds);
             PFrag<C> pf;
-            qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb, qlds);
-            pv<C, true, 0>(cx, vb, pf, st, cb, vlds);
-        }
-        // the V staging tiles are free once every wave is past its last P*V
-        float* obuf = reinterpret_cast<float*>(smem);  // [2][ROWS_PAD][OPITCH], then [8][ROWS_PAD]
-        finish_task<C>(a, cx, st, part, vscale, obuf, obuf + C::ROWS_PAD * C::OPITCH,
-                       obuf + 2 * C::ROWS_PAD * C::OPITCH);
+            qk_softmax<C, M>(a, cx, qf, kb, st, pf, cb, qlds);
+            sp = slice_pages<C>(a, cx, pc, tile + 1);
+            load_k<C>(a, cx, sp, kb);
+            pv<C, M, C::KVMEM>(cx, vb, pf, st, cb, vlds);
+            cb += kTileTokens;
+            ++tile;
+        };
+        if constexpr (C::WIN)
+            for (; tile < F0 && tile + 1 < T1;) step(Masked{});  // window head
+        for (; tile < F1 && tile + 1 < T1;) step(Full{});        // the bulk
+        if constexpr (C::WIN)
+            for (; tile + 1 < T1;) step(Masked{});               // causal boundary
+        dma_fence<C>();
+        load_v<C>(a, cx, sp, vb, vlds);
+        PFrag<C> pf;
+        qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb, qlds);
+        pv<C, true, 0>(cx, vb, pf, st, cb, vlds);
     }
+    // the V tiles are free once every wave is past its last P*V (the merge's
+    // first barrier)
+    float* obuf = reinterpret_cast<float*>(smem);  // [2][ROWS_PAD][OPITCH], then [8][ROWS_PAD]
+    finish_task<C>(a, cx, st, part, vscale, obuf, obuf + C::ROWS_PAD * C::OPITCH, obuf + 2 * C::ROWS_PAD * C::OPITCH);
 }
 
 // ------------------------------------------------------------- merge kernel
@@ -1559,7 +1444,6 @@ using TileFn = void (*)(const TileArgs);
 struct Entry {
     KernelKey key;
     TileFn fn;
-    bool segments;  // runs a list of tasks per workgroup (whole-stage prefetch instances)
 };
 
 // Kernel instances are compiled in shards (PA_SHARD 0..3, one object file
@@ -1573,9 +1457,8 @@ struct Entry {
 #define PA_IN_SHARD(n) (PA_SHARD == -1 || PA_SHARD == (n))
 
 #define PA_E(KV, SC, VT, D, PG, NT, QF, W) PA_EM(KV, SC, VT, D, PG, NT, QF, 0, W)
-#define PA_EM(KV, SC, VT, D, PG, NT, QF, MXS, W)                      \
-    {{KV, SC, VT, D, PG, NT, QF, MXS, W}, &pa_tile_kernel<Cfg<KV, SC, VT, D, PG, NT, QF, MXS, W>>, \
-     Cfg<KV, SC, VT, D, PG, NT, QF, MXS, W>::PF}
+#define PA_EM(KV, SC, VT, D, PG, NT, QF, MXS, W) \
+    {{KV, SC, VT, D, PG, NT, QF, MXS, W}, &pa_tile_kernel<Cfg<KV, SC, VT, D, PG, NT, QF, MXS, W>>}
 #define PA_PG(KV, SC, VT, D, NT, W) \
     PA_E(KV, SC, VT, D, 16, NT, 0, W), PA_E(KV, SC, VT, D, 64, NT, 0, W), PA_E(KV, SC, VT, D, 128, NT, 0, W)
 #define PA_NT(KV, SC, VT, D, W) PA_PG(KV, SC, VT, D, 1, W), PA_PG(KV, SC, VT, D, 2, W)
@@ -1626,11 +1509,6 @@ static const Entry* find_entry(const KernelKey& k) {
 static TileFn find(const KernelKey& k) {
     const Entry* e = find_entry(k);
     return e ? e->fn : nullptr;
-}
-
-bool tile_runs_segments(const KernelKey& key) {
-    const Entry* e = find_entry(key);
-    return e && e->segments;
 }
 
 bool have_tile_kernel(const KernelKey& key) { return find(key) != nullptr; }

@@ -281,70 +281,3 @@ def test_static_decode_refuses_partials_beyond_its_buffer_before_the_device():
     msg = B.pa_last_error()
     assert "static scratch" in msg and "partitions" in msg, msg
 
-
-def _seg_problem(lens, **kw):
-    base = dict(num_seqs=len(lens), qlen=1, num_kv_heads=2, q_per_kv=8, head_dim=256, page_size=16,
-                num_blocks=100000, max_blocks_per_seq=2100, max_context_len=max(lens), kv_dtype="fp8",
-                scale_mode="token")
-    base.update(kw)
-    return B.make_problem(**base)
-
-
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_segment_plan_covers_every_tile_once_and_balances_workgroups(seed):
-    """fp8 per-token caches with 16 query rows (the whole-stage-prefetch
-    instances): a few long sequences are cut into one contiguous chunk of the
-    concatenated (sequence, KV head) tile ranges per workgroup slot. Every
-    owned tile is read exactly once, each (sequence, KV head)'s partitions are
-    numbered in tile order from 0, partial units do not overlap, and every
-    workgroup's tiles plus one per extra range (a switch costs about a tile)
-    stay within the plan's per-workgroup target, which is within a few tiles
-    of an even share."""
-    g = torch.Generator().manual_seed(seed)
-    lens = torch.randint(2048, 32769, (16,), generator=g).tolist()
-    lens[3] = 0  # an empty sequence: one empty task, rows written as zeros
-    p = _seg_problem(lens)
-    tasks, parts, info, offs = B.pa_plan_host(p, lens, num_cus=256, blocks_per_cu=1, with_offsets=True)
-    H = p.num_kv_heads
-    W = info.num_workgroups
-    assert W <= 256 and info.num_tasks > W  # chunks span several ranges
-    T = info.tiles_per_task
-    offs = offs.tolist()
-    assert offs[0] == 0 and offs[-1] == info.num_tasks and all(a <= b for a, b in zip(offs, offs[1:]))
-    total = sum((L + 255) // 256 for L in lens) * H
-    seen, order = set(), {}
-    for w in range(W):
-        ntiles = 0
-        for b, kp, t0, t1 in tasks[offs[w]:offs[w + 1]].tolist():
-            kvh, part = kp & 0xFFFF, kp >> 16
-            assert part == order.get((b, kvh), 0)  # partitions in tile order
-            order[(b, kvh)] = part + 1
-            for t in range(t0, t1):
-                assert (b, kvh, t) not in seen
-                seen.add((b, kvh, t))
-            ntiles += t1 - t0
-        ranges = sum(1 for r in tasks[offs[w]:offs[w + 1]].tolist() if r[3] > r[2])  # empty tasks stream nothing
-        assert ntiles + ranges - 1 <= T or ntiles == 0
-    assert len(seen) == total
-    assert T <= (total + 255) // 256 + 3
-    units = set()
-    for b in range(len(lens)):
-        for kvh in range(H):
-            P, u0 = parts[b * H + kvh].tolist()
-            assert P == order[(b, kvh)]
-            if P > 1:
-                assert not units & set(range(u0, u0 + P))
-                units |= set(range(u0, u0 + P))
-            else:
-                assert u0 == -1
-    assert info.total_parts == len(units) and info.merge_needed == (len(units) > 0)
-
-
-def test_segment_plan_only_for_the_prefetch_instances():
-    lens = [30000, 20000, 9000]
-    info = B.pa_plan_host(_seg_problem(lens), lens, num_cus=64, blocks_per_cu=1)[2]
-    assert info.num_tasks > info.num_workgroups  # workgroups run several ranges
-    # 32 query rows (qlen 4), or bf16, or a transposed V: one task per workgroup
-    for kw in (dict(qlen=4), dict(kv_dtype="bf16", scale_mode="none"), dict(v_layout="trans")):
-        info = B.pa_plan_host(_seg_problem(lens, **kw), lens, num_cus=64, blocks_per_cu=1)[2]
-        assert info.num_workgroups == info.num_tasks, kw
