@@ -57,6 +57,7 @@ class Spec:
     pad_cols: int = 2
     causal: int = 0  # 1: query token i attends to t < L - qlen + i + 1
     window: int = 0  # > 0: sliding window of that many tokens ending there
+    mx_k_scale: tuple = (118, 136)  # MXFP4: K scale bytes drawn uniformly from [lo, hi]
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -138,6 +139,15 @@ MXFP4_SHORT_Q8 = _spec("mxfp4_p128_b16_l2048_qfp8", num_seqs=16, lens=("const", 
 MXFP4_SHORT_QBF = MXFP4_SHORT_Q8.replace(name="mxfp4_p128_b16_l2048_qbf16", q_dtype="bf16", seed=1007)
 MXFP4_LONG_Q8 = MXFP4_SHORT_Q8.replace(name="mxfp4_p128_b16_l131072_qfp8", lens=("const", 131072), seed=1008)
 MXFP4_LONG_QBF = MXFP4_LONG_Q8.replace(name="mxfp4_p128_b16_l131072_qbf16", q_dtype="bf16", seed=1009)
+
+# The MXFP4 workloads' scale bytes put logits in the thousands, so their softmax
+# is one-hot. These two draw K scale bytes from [122, 127] instead: logits of
+# standard deviation about 1.4 and about 50 tokens of effective weight per row,
+# so every step of the softmax and the weighted V sum shows in the output.
+MXFP4_SPREAD_Q8 = MXFP4_SHORT_Q8.replace(name="mxfp4_p128_b16_l2048_qfp8_kscale122-127", mx_k_scale=(122, 127),
+                                         seed=1020)
+MXFP4_SPREAD_QBF = MXFP4_SPREAD_Q8.replace(name="mxfp4_p128_b16_l2048_qbf16_kscale122-127", q_dtype="bf16",
+                                           seed=1021)
 
 # Masked variants: a 1024-token sliding window on the bf16 batch, and causal
 # multi-token verification (qlen 4) on the fp8 per-token batch.
@@ -290,8 +300,8 @@ def make_case(spec: Spec, fill: Optional[str] = None, seed: Optional[int] = None
     elif spec.kv_dtype == "mxfp4":
         K = torch.randint(0, 256, (num_blocks, H, PG, D // 2), generator=g, dtype=torch.int32).to(torch.uint8)
         V = torch.randint(0, 256, (num_blocks, H, PG, D // 2), generator=g, dtype=torch.int32).to(torch.uint8)
-        k_scale = torch.randint(118, 137, (num_blocks, H, PG, D // 32), generator=g, dtype=torch.int32).to(
-            torch.uint8)
+        k_scale = torch.randint(spec.mx_k_scale[0], spec.mx_k_scale[1] + 1, (num_blocks, H, PG, D // 32),
+                                generator=g, dtype=torch.int32).to(torch.uint8)
         v_scale = torch.randint(118, 137, (num_blocks, H, PG, D // 32), generator=g, dtype=torch.int32).to(
             torch.uint8)
     else:

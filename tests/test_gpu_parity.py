@@ -172,6 +172,27 @@ def test_mxfp4_scaled_qk_near_tie_exceeds_the_element_bound():
     assert finite and rel <= REL_L2 and worst > 1.0
 
 
+@pytest.mark.parametrize("scaled", [0, 1], ids=["exact_qk", "scaled_qk"])
+@pytest.mark.parametrize("spec", [I.MXFP4_SPREAD_Q8, I.MXFP4_SPREAD_QBF], ids=lambda s: s.name)
+def test_mxfp4_spread_softmax(spec, scaled):
+    """MXFP4 with K scale bytes in [122, 127]: logits of order 1, so the
+    softmax spreads over many tokens instead of being one-hot, and every step
+    (the weights, their bf16 hi + lo parts, the weighted V sum, the partition
+    merge) shows in the output. Full size (16 sequences x 2048 tokens x 4 KV
+    heads), every sequence against the oracle, planned, split and plan-free,
+    with both QK forms; poison invariant."""
+    case = I.make_case(spec)
+    ref = oracle.pa_decode(case)
+    out, _ = run(case, mxfp4_scaled_qk=scaled)
+    check_parity(out, ref, what=spec.name + (" scaled QK" if scaled else ""))
+    many, _ = run(case, mxfp4_scaled_qk=scaled, task_budget=100000)
+    check_parity(many, ref, what=spec.name + " many partitions")
+    if not scaled:
+        check_parity(run_direct(case), ref, what=spec.name + " plan-free")
+    zero = run(I.refill(case, "zero"), mxfp4_scaled_qk=scaled)[0]
+    assert torch.equal(zero.view(torch.int16), out.view(torch.int16))
+
+
 # ------------------------------------------------------------- plan-free path
 
 def run_direct(case, fill_out=float("nan")):

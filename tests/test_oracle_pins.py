@@ -229,6 +229,9 @@ TINY_SPECS = [
     I.Spec("t_fp8_token_p64", 2, ("fixed", (64, 150)), 1, 1, 8, 128, 64, "fp8", "token", seed=16),
     I.Spec("t_mxfp4_qfp8", 2, ("fixed", (130, 255)), 1, 2, 4, 128, 128, "mxfp4", q_dtype="fp8", seed=17),
     I.Spec("t_mxfp4_qbf16", 2, ("fixed", (1, 260)), 1, 1, 16, 128, 128, "mxfp4", q_dtype="bf16", seed=18),
+    # K scale bytes in [122, 127]: logits of order 1, a softmax spread over many tokens
+    I.Spec("t_mxfp4_qfp8_spread", 2, ("fixed", (200, 385)), 1, 2, 4, 128, 128, "mxfp4", q_dtype="fp8", seed=19,
+           mx_k_scale=(122, 127)),
 ]
 
 
@@ -240,16 +243,21 @@ def test_oracle_equals_brute_force_dense(spec):
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
 
 
-@pytest.mark.parametrize("spec", TINY_SPECS[:1] + TINY_SPECS[3:5] + TINY_SPECS[6:7], ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", TINY_SPECS[:1] + TINY_SPECS[3:5] + TINY_SPECS[6:7] + TINY_SPECS[8:9],
+                         ids=lambda s: s.name)
 def test_negative_controls_are_caught(spec):
     """Plausible mistakes in a reference fail the brute-force comparison."""
     case = I.make_case(spec)
     got = oracle.pa_decode(case)
     if case.kv_dtype == "mxfp4":
-        # this workload's logits are in the thousands, so softmax is one-hot and
-        # a 5 % scale error is invisible; a swapped nibble order is not
+        # a swapped nibble order is caught on any MXFP4 case; a 5 % scale error
+        # only where the softmax is not one-hot (the workload recipe's scale
+        # bytes put logits in the thousands)
         bad = dense_reference(case, nibble_swap=True)
         assert not np.allclose(got, bad, rtol=1e-6, atol=1e-9)
+        if spec.mx_k_scale != (118, 136):
+            bad_scale = dense_reference(case, sigma_mult=1.05)
+            assert not np.allclose(got, bad_scale, rtol=1e-6, atol=1e-9)
     else:
         bad_scale = dense_reference(case, sigma_mult=1.05)
         assert not np.allclose(got, bad_scale, rtol=1e-6, atol=1e-9)
