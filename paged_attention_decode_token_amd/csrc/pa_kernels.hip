@@ -251,9 +251,14 @@ struct Cfg {
     static constexpr bool PF = VDMA && KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 1;
     // query fragments in LDS (one copy per workgroup) instead of registers
     static constexpr bool QLDS = NT2_DMA || NT4;
-    static constexpr int VPITCH = D * 2 + 16;                        // staged bf16 row pitch in bytes
+    // register-staged V tile (bf16 rows): row pitch, extra offset per group of
+    // 8 rows, and a gap after every 2^VGSH chunks of a row, in bytes (sv_row, sv_chunk)
+    static constexpr int VPITCH = D == 256 ? 544 : KV == KV_BF16 ? 288 : KV == KV_MXFP4 ? 320 : 272;
+    static constexpr int VGRP = D == 256 || KV == KV_BF16 ? 128 : KV == KV_MXFP4 ? 32 : 0;
+    static constexpr int VGAP = D == 256 || KV == KV_MXFP4 ? 16 : 0;
+    static constexpr int VGSH = D == 256 ? 4 : 2;
     static constexpr int CPR = ROWB / 16;                            // 16-byte chunks per V row (DMA)
-    static constexpr int VSTAGE_BYTES = VDMA ? 64 * ROWB : (STAGE_V ? 32 * VPITCH : 0);  // per wave
+    static constexpr int VSTAGE_BYTES = VDMA ? 64 * ROWB : (STAGE_V ? 32 * VPITCH + 3 * VGRP : 0);  // per wave
     static constexpr int SCALE_BYTES = PF ? 512 : 0;                 // K then V scales of 64 tokens (fp32)
     static constexpr int WAVE_LDS = (PF ? 2 : 1) * (VSTAGE_BYTES + SCALE_BYTES);  // per wave
     static constexpr int QLDS_BYTES = QLDS ? NT * KSTEPS * 64 * 16 : 0;
@@ -291,6 +296,34 @@ PA_DEV int vswz(int r) {
     else if constexpr (C::ROWB >= 256) return (r & 7) | (((r >> 4) & 1) << 3);
     else return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
 }
+
+// Layout of the register-staged V tile: bf16 rows of D / 8 chunks of 16
+// bytes; row e (= 8 g + token within the step's 8-token half) holds chunk k at
+// byte sv_row(e) + sv_chunk(k). The offsets are the lane's base plus constants, and both
+// sides avoid LDS bank conflicts (64 banks of 4 bytes):
+//   the PV reads (ds_read_b64_tr_b16): a half-wave reads chunks 2dt and
+//     2dt + 1 of rows 8g + [0, 4) (+ 4) for g in {2h, 2h + 1}: the row pitch
+//     and the per-8-row offset put those 8 rows in 8 different 32-byte bank
+//     windows;
+//   the staging writes (16 bytes a lane): a 16-lane pass writes chunks c v + j
+//     (c = 1, 2 or 4 chunks a lane) of 16 / (D / 8 / c) consecutive rows; the
+//     gap inside a row keeps chunks 256 bytes apart (head_dim 256) or a
+//     lane's 4 chunks (MXFP4) off each other's banks.
+// Conflict-free both ways for bf16 and MXFP4 at head_dim 128 and for head_dim
+// 256; fp8 at head_dim 128 keeps 2-way reads (no pitch of this form clears
+// both its reads and its writes).
+template <class C>
+PA_DEV int sv_row(int e) {
+    return e * C::VPITCH + (e >> 3) * C::VGRP;
+}
+template <class C>
+PA_DEV int sv_chunk(int k) {
+    return 16 * k + C::VGAP * (k >> C::VGSH);
+}
+// Callers split both terms into the lane's part and a compile-time part: with
+// a power-of-two count of rows per load instruction, (i TPI + l) >> 3 =
+// ((i TPI) >> 3) + (l >> 3) for l < TPI, and a lane's c chunks (c <= 2^VGSH,
+// starting at a multiple of c) never straddle a gap.
 
 template <class C>
 struct State {
@@ -868,32 +901,37 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         if constexpr (C::STAGE_V) {
-            // stage rows e of step s into the wave's LDS tile (bf16, row pitch VPITCH);
-            // rows of tokens at or past L are written as zeros
+            // stage rows e of step s into the wave's LDS tile (bf16, row pitch VPITCH,
+            // chunks placed by sv_row and sv_chunk); rows of tokens at or past L, or before
+            // every row's window, are written as zeros
             const int vseg = lane % C::LPR;
+            const int lrow = lane / C::LPR;  // < TPI
+            constexpr int CPL = C::KV == KV_BF16 ? 1 : C::KV == KV_FP8 ? 2 : 4;  // bf16 chunks a lane
+            char* dst = vlds + sv_row<C>(lrow) + sv_chunk<C>(CPL * vseg);
 #pragma unroll
             for (int i = 0; i < C::IPS; ++i) {
-                const int e = i * C::TPI + lane / C::LPR;
+                const int e = i * C::TPI + lrow;
                 const int t = 16 * (e >> 3) + 8 * s + (e & 7);
                 const bool ok = !MASK || (cb + t < cx.L && (!C::WIN || cb + t >= cx.s_lo));
-                char* dst = vlds + e * C::VPITCH;
+                // row e = i TPI + lrow: sv_row(e) = sv_row(lrow) + this constant
+                char* row = dst + (i * C::TPI) * C::VPITCH + ((i * C::TPI) >> 3) * C::VGRP;
                 u32x4 raw = vb.v[s][i];
                 if constexpr (C::KV == KV_BF16) {
                     if (!ok) raw = u32x4{0, 0, 0, 0};
-                    *reinterpret_cast<u32x4*>(dst + 16 * vseg) = raw;
+                    *reinterpret_cast<u32x4*>(row) = raw;
                 } else if constexpr (C::KV == KV_FP8) {
                     if (!ok) raw = u32x4{0, 0, 0, 0};
                     u32x2 a0 = fp8x4_to_bf16x4(raw[0]), a1 = fp8x4_to_bf16x4(raw[1]);
                     u32x2 a2 = fp8x4_to_bf16x4(raw[2]), a3 = fp8x4_to_bf16x4(raw[3]);
-                    *reinterpret_cast<u32x4*>(dst + 32 * vseg) = u32x4{a0[0], a0[1], a1[0], a1[1]};
-                    *reinterpret_cast<u32x4*>(dst + 32 * vseg + 16) = u32x4{a2[0], a2[1], a3[0], a3[1]};
+                    *reinterpret_cast<u32x4*>(row) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                    *reinterpret_cast<u32x4*>(row + 16) = u32x4{a2[0], a2[1], a3[0], a3[1]};
                 } else {
                     const float vsf = e8m0_to_f32((vb.vsc[s][i] >> (8 * vseg)) & 0xFFu);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         u32x4 w = fp4x8_to_bf16x8(raw[j], vsf);
                         if (!ok) w = u32x4{0, 0, 0, 0};
-                        *reinterpret_cast<u32x4*>(dst + 64 * vseg + 16 * j) = w;
+                        *reinterpret_cast<u32x4*>(row + 16 * j) = w;
                     }
                 }
             }
@@ -973,8 +1011,13 @@ PA_DEV void pv(const Ctx& cx, const VBuf<C>& vb, const PFrag<C>& pf, State<C>& s
         for (int dt = 0; dt < C::DT; ++dt) {
             bf16x8 va;
             if constexpr (C::STAGE_V) {
-                // A lane (m = d offset, g) needs rows 8g + [0, 8) at column 16dt + m
-                const char* base = vlds + (8 * lg + (ln >> 2)) * C::VPITCH + 2 * (16 * dt + 4 * (ln & 3));
+                // A lane (m = d offset, g) needs rows 8g + [0, 8) at column 16dt + m:
+                // source lane ln reads row 8g + (ln >> 2) (+ 4), columns
+                // 16dt + 4 (ln & 3) + [0, 4), i.e. half ln & 1 of chunk 2dt + ((ln & 3) >> 1)
+                // sv_row(8 g + (ln >> 2)) and sv_chunk(2 dt + c), c < 2, as lane part
+                // plus constant
+                const char* base = vlds + (8 * lg + (ln >> 2)) * C::VPITCH + lg * C::VGRP + 16 * ((ln & 3) >> 1) +
+                                   8 * (ln & 1) + sv_chunk<C>(2 * dt);
                 bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                     (__attribute__((address_space(3))) bf16x4*)(base));
                 bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
