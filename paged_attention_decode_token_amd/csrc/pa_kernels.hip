@@ -57,6 +57,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define PA_DEV __device__ __forceinline__
 
+// Online softmax: how far (base 2) a row's max may grow past the reference
+// max before the weights are re-based and O rescaled. Weights stay below
+// 2^kRescaleLog2 = 256, well inside bf16 and fp32 range.
+constexpr float kRescaleLog2 = 8.f;
+
 // ------------------------------------------------------------------ helpers
 
 PA_DEV u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -249,6 +254,14 @@ struct Cfg {
     // LDS DMA, so register loads cannot be kept in flight across a DMA wait;
     // hence the one full wait at the top.)
     static constexpr bool PF = VDMA && KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 1;
+    // Lazy softmax rescaling (qk_softmax) in the whole-stage-prefetch
+    // instances, where it measured faster (fp8 per-token qlen 1: 71.0 -> 70.3
+    // us per call). With more than one N tile the register allocation around
+    // its branch spills in the loops of the head_dim-256 and 64-row
+    // instances; in the other one-tile instances it measured no faster, and
+    // at bf16 page 128 its smaller register count lets a second workgroup in,
+    // which is slower there.
+    static constexpr bool LAZY = PF;
     // query fragments in LDS (one copy per workgroup) instead of registers
     static constexpr bool QLDS = NT2_DMA || NT4;
     // register-staged V tile (bf16 rows): row pitch, extra offset per group of
@@ -777,9 +790,45 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
             tvs[i] = (!MASK || (tok < cx.L && (!C::WIN || tok >= cx.s_lo))) ? kb.tvs[i] : 0.f;
         }
     }
+    // The weights of N tile nt against the reference max muse: P (times the
+    // per-token V scale) rounded to bf16 into pf, and their sum as l
+    // accumulates it (returned in lsum).
+#define PA_WEIGHTS(nt, muse, lsum)                                                                    \
+    {                                                                                                 \
+        uint32_t pw[8], plo[8];                                                                       \
+        _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                               \
+            float p[4];                                                                               \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j) p[j] = fast_exp2(acc[c][nt][j] - (muse));   \
+            /* the weight sum: of P in fp32 where PV's weights are not the bf16 P itself */           \
+            if constexpr (C::PSPLIT || C::SC == SC_TOKEN) lsum += (p[0] + p[1]) + (p[2] + p[3]);      \
+            /* the PV weight: P times the token's V scale in fp32, rounded once */                    \
+            if constexpr (C::SC == SC_TOKEN) {                                                        \
+                _Pragma("unroll") for (int j = 0; j < 4; ++j) p[j] *= tvs[4 * c + j];                 \
+            }                                                                                         \
+            const uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);                    \
+            if constexpr (C::PSPLIT) {                                                                \
+                plo[2 * c] = pack_bf16(p[0] - bf16_lo(w0), p[1] - bf16_hi(w0));                       \
+                plo[2 * c + 1] = pack_bf16(p[2] - bf16_lo(w1), p[3] - bf16_hi(w1));                   \
+            } else if constexpr (C::SC != SC_TOKEN) {                                                 \
+                /* the weight sum of exactly the rounded weights PV uses */                           \
+                lsum += (bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1));                    \
+            }                                                                                         \
+            pw[2 * c] = w0;                                                                           \
+            pw[2 * c + 1] = w1;                                                                       \
+        }                                                                                             \
+        /* step s uses calls 2s (tokens 16lg + 8s + 0..3) and 2s + 1 (16lg + 8s + 4..7) */            \
+        pf.hi[0][nt] = u32x4{pw[0], pw[1], pw[2], pw[3]};                                             \
+        pf.hi[1][nt] = u32x4{pw[4], pw[5], pw[6], pw[7]};                                             \
+        if constexpr (C::PSPLIT) {                                                                    \
+            pf.lo[0][nt] = u32x4{plo[0], plo[1], plo[2], plo[3]};                                     \
+            pf.lo[1][nt] = u32x4{plo[4], plo[5], plo[6], plo[7]};                                     \
+        }                                                                                             \
+    }
+    float mloc[NT];
+    bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        float mloc = -__builtin_inff();
+        mloc[nt] = -__builtin_inff();
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -791,51 +840,52 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
                 // select, never a multiply
                 if (MASK) x = (cb + t >= cx.row_s[nt] && cb + t < cx.row_e[nt]) ? x : -__builtin_inff();
                 acc[c][nt][j] = x;
-                mloc = fmaxf(mloc, x);
+                mloc[nt] = fmaxf(mloc[nt], x);
             }
-        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
-        const float mnew = fmaxf(st.m[nt], mloc);
-        const float muse = (mnew == -__builtin_inff()) ? 0.f : mnew;
-        const float alpha = fast_exp2(st.m[nt] - muse);
-        st.m[nt] = mnew;
-        float lsum = 0.f;
-        uint32_t pw[8], plo[8];
+        mloc[nt] = fmaxf(mloc[nt], shfl_xor(mloc[nt], 16));
+        mloc[nt] = fmaxf(mloc[nt], shfl_xor(mloc[nt], 32));
+        if constexpr (C::LAZY) {
+            grow = grow || mloc[nt] > st.m[nt] + kRescaleLog2;
+        } else {
+            // re-based every slice
+            const float mnew = fmaxf(st.m[nt], mloc[nt]);
+            const float muse = (mnew == -__builtin_inff()) ? 0.f : mnew;
+            const float alpha = fast_exp2(st.m[nt] - muse);
+            st.m[nt] = mnew;
+            float lsum = 0.f;
+            PA_WEIGHTS(nt, muse, lsum)
+            st.l[nt] = st.l[nt] * alpha + lsum;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float p[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[j] = fast_exp2(acc[c][nt][j] - muse);
-            // the weight sum: of P in fp32 where PV's weights are not the bf16
-            // P itself (hi + lo parts, or P times a per-token V scale)
-            if constexpr (C::PSPLIT || C::SC == SC_TOKEN) lsum += (p[0] + p[1]) + (p[2] + p[3]);
-            // the PV weight: P times the token's V scale in fp32, rounded once
-            if constexpr (C::SC == SC_TOKEN) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) p[j] *= tvs[4 * c + j];
-            }
-            const uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);
-            if constexpr (C::PSPLIT) {
-                plo[2 * c] = pack_bf16(p[0] - bf16_lo(w0), p[1] - bf16_hi(w0));
-                plo[2 * c + 1] = pack_bf16(p[2] - bf16_lo(w1), p[3] - bf16_hi(w1));
-            } else if constexpr (C::SC != SC_TOKEN) {
-                // the weight sum of exactly the rounded weights PV uses
-                lsum += (bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1));
-            }
-            pw[2 * c] = w0;
-            pw[2 * c + 1] = w1;
+            for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] *= alpha;
         }
-        st.l[nt] = st.l[nt] * alpha + lsum;
-        // step s uses calls 2s (tokens 16lg + 8s + 0..3) and 2s + 1 (16lg + 8s + 4..7)
-        pf.hi[0][nt] = u32x4{pw[0], pw[1], pw[2], pw[3]};
-        pf.hi[1][nt] = u32x4{pw[4], pw[5], pw[6], pw[7]};
-        if constexpr (C::PSPLIT) {
-            pf.lo[0][nt] = u32x4{plo[0], plo[1], plo[2], plo[3]};
-            pf.lo[1][nt] = u32x4{plo[4], plo[5], plo[6], plo[7]};
-        }
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] *= alpha;
     }
+    if constexpr (C::LAZY) {
+        // Lazy rescaling: the reference max m of a row moves only on slices
+        // where some row of the wave has seen its max grow past
+        // m + kRescaleLog2 (one wave-uniform branch); otherwise the weights are
+        // taken against the old m, at most 2^kRescaleLog2, and l and O are left
+        // alone. (m, l, O) describe the same result either way; the per-element
+        // rescale of O then runs on few slices instead of every one.
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float mnew = fmaxf(st.m[nt], mloc[nt]);
+                const float alpha = fast_exp2(st.m[nt] - ((mnew == -__builtin_inff()) ? 0.f : mnew));
+                st.m[nt] = mnew;
+                st.l[nt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) st.o[dt][nt] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const float muse = (st.m[nt] == -__builtin_inff()) ? 0.f : st.m[nt];
+            float lsum = 0.f;
+            PA_WEIGHTS(nt, muse, lsum)
+            st.l[nt] += lsum;
+        }
+    }
+#undef PA_WEIGHTS
 }
 
 // Workgroup barrier ordering LDS accesses only. __syncthreads also waits for
