@@ -78,7 +78,9 @@ def kernel_tag_of(spec) -> str:
     rows = spec.qlen * spec.q_per_kv
     nt = 1 if rows <= 16 else (2 if rows <= 32 else 4)
     qf = 1 if spec.q_dtype == "fp8" else 0
-    win = 1 if spec.window > 0 or (spec.causal and spec.qlen > 1) else 0
+    # a window: 1; causal rows without one: 2 for fp8 per-token caches (the
+    # causal-only instances), 1 otherwise
+    win = 1 if spec.window > 0 else (0 if not (spec.causal and spec.qlen > 1) else (2 if sc == 2 and kv == 1 else 1))
     return "Cfg<%d, %d, %d, %d, %d, %d, %d, 0, %d>" % (kv, sc, vt, spec.head_dim, spec.page_size, nt, qf, win)
 
 

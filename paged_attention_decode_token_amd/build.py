@@ -31,10 +31,10 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    # the kernel instances are compiled in four shards (see the dispatch section
+    # the kernel instances are compiled in five shards (see the dispatch section
     # of pa_kernels.hip), in parallel with the host code
     kern = os.path.join(CSRC, "pa_kernels.hip")
-    jobs = [(kern, os.path.join(bdir, "pa_kernels.%d.o" % i), ["-DPA_SHARD=%d" % i]) for i in range(4)]
+    jobs = [(kern, os.path.join(bdir, "pa_kernels.%d.o" % i), ["-DPA_SHARD=%d" % i]) for i in range(5)]
     jobs.append((os.path.join(CSRC, "pa_kv_write.hip"), os.path.join(bdir, "pa_kv_write.o"), []))
     # the MQA-logits kernel reads every MFMA result at once: keep the results in
     # ordinary VGPRs instead of accumulator registers (no per-element copies)

@@ -143,7 +143,11 @@ pa::KernelKey key_of(const pa_problem& p) {
     k.ntiles_n = rows_of(p) <= 16 ? 1 : (rows_of(p) <= 32 ? 2 : 4);
     k.q_fp8 = p.q_dtype == PA_Q_FP8_E4M3 ? 1 : 0;
     k.mx_scaled = (p.kv_dtype == PA_KV_MXFP4 && p.mxfp4_scaled_qk) ? 1 : 0;
-    k.win = (p.window > 0 || (p.causal && p.qlen > 1)) ? 1 : 0;  // qlen 1: causal is the plain decode
+    // 1: a sliding window; 2: causal rows without one (qlen 1: causal is the
+    // plain decode), served by the windowed instances where no causal-only
+    // instance is compiled
+    k.win = p.window > 0 ? 1 : ((p.causal && p.qlen > 1) ? 2 : 0);
+    if (k.win == 2 && !pa::have_tile_kernel(k)) k.win = 1;
     return k;
 }
 

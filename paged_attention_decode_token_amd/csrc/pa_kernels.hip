@@ -167,9 +167,15 @@ struct BoolTag {
 
 template <int KV_, int SC_, int VT_, int D_, int PG_, int NT_, int QF8_, int MXS_, int WIN_>
 struct Cfg {
-    // causal rows or a sliding window: masked tiles may also open the range
-    // (the window's first tiles) and close it before the context boundary
-    static constexpr bool WIN = WIN_ != 0;
+    // WIN_ 1: a sliding window (with or without causal rows): masked tiles may
+    // open the range (the window's first tiles, with the rows before the
+    // window inert) and close it before the context boundary. WIN_ 2: causal
+    // rows without a window: each row ends at its own position, at most
+    // qlen - 1 tokens before L, so every score gets a select against the row's
+    // end (no V byte past it is unowned), and only the last tile runs masked.
+    static constexpr bool WIN = WIN_ == 1;
+    static constexpr bool ROWS = WIN_ != 0;    // per-row range ends
+    static constexpr bool CAUSAL = WIN_ == 2;  // the select in unmasked tiles
     static constexpr int KV = KV_;
     static constexpr int SC = SC_;
     static constexpr bool VT = VT_ != 0;
@@ -229,7 +235,7 @@ struct Cfg {
     // every load in flight (qlen 4, batch 16: 82-87 against 90-118 us per call).
     // The plain page-16 and page-128 instances keep register staging, whose
     // loops do not spill and which measured faster there (80-81 against 99 us).
-    static constexpr bool NT2_DMA = KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 2 && D_ == 256 && (WIN_ != 0 || PG_ == 64);
+    static constexpr bool NT2_DMA = KV_ == KV_FP8 && SC_ == SC_TOKEN && NT_ == 2 && D_ == 256 && (WIN_ == 1 || PG_ == 64);
     // 64 query rows (four N tiles, head_dim 128 only): the accumulators alone
     // take 128 registers, so V always goes by LDS DMA and the query fragments
     // live in LDS, leaving the registers to K, the scores and O.
@@ -839,6 +845,7 @@ PA_DEV void qk_softmax(const TileArgs& a, const Ctx& cx, const QFrag<C>& qf, con
                 // outside the row's causal / window range, or at or past L: -inf by a
                 // select, never a multiply
                 if (MASK) x = (cb + t >= cx.row_s[nt] && cb + t < cx.row_e[nt]) ? x : -__builtin_inff();
+                else if (C::CAUSAL) x = cb + t < cx.row_e[nt] ? x : -__builtin_inff();
                 acc[c][nt][j] = x;
                 mloc[nt] = fmaxf(mloc[nt], x);
             }
@@ -1166,7 +1173,7 @@ PA_DEV Range task_range(const TileArgs& a, const TaskTiles& tt, Ctx& cx, int par
     // with a sliding window, else 0.
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
-        if constexpr (C::WIN) {
+        if constexpr (C::ROWS) {
             const int r = 16 * nt + cx.ln;
             const int i = r < a.rows ? r / a.q_per_kv : a.qlen - 1;
             const int e = a.causal ? L - a.qlen + i + 1 : L;
@@ -1177,7 +1184,9 @@ PA_DEV Range task_range(const TileArgs& a, const TaskTiles& tt, Ctx& cx, int par
             cx.row_s[nt] = 0;
         }
     }
-    const int e_min = C::WIN ? max(0, a.causal ? L - a.qlen + 1 : L) : L;  // smallest row end
+    // smallest row end (causal-only instances select every score against its
+    // row's end instead, so their unmasked tiles run to the last one)
+    const int e_min = C::WIN ? max(0, a.causal ? L - a.qlen + 1 : L) : L;
     const int s_min = C::WIN && a.window > 0 ? max(0, e_min - a.window) : 0;
     const int s_max = C::WIN && a.window > 0 ? max(0, L - a.window) : 0;
     // plan-free partitions count their tiles from the window's first tile
@@ -1539,10 +1548,11 @@ struct Entry {
     TileFn fn;
 };
 
-// Kernel instances are compiled in shards (PA_SHARD 0..3, one object file
+// Kernel instances are compiled in shards (PA_SHARD 0..4, one object file
 // each, built in parallel); without PA_SHARD one object holds them all.
 //   0: bf16 and MXFP4, plain decode      1: bf16 with causal rows / a window
-//   2: e4m3 caches, plain decode         3: e4m3 with causal rows / a window
+//   2: e4m3 caches, plain decode         3: e4m3 with a window (or causal rows)
+//   4: e4m3 with per-token scales, causal rows without a window
 // Shard 0 also holds the merge kernel and the dispatch functions.
 #ifndef PA_SHARD
 #define PA_SHARD -1
@@ -1581,14 +1591,19 @@ extern const Entry kShard3[] = {PA_VT(KV_FP8, SC_TENSOR, 1), PA_VT(KV_FP8, SC_TO
 extern const int kShard3Size = sizeof(kShard3) / sizeof(kShard3[0]);
 #endif
 
+#if PA_IN_SHARD(4)
+extern const Entry kShard4[] = {PA_VT(KV_FP8, SC_TOKEN, 2)};
+extern const int kShard4Size = sizeof(kShard4) / sizeof(kShard4[0]);
+#endif
+
 #if PA_IN_SHARD(0)
-extern const Entry kShard1[], kShard2[], kShard3[];
-extern const int kShard1Size, kShard2Size, kShard3Size;
+extern const Entry kShard1[], kShard2[], kShard3[], kShard4[];
+extern const int kShard1Size, kShard2Size, kShard3Size, kShard4Size;
 
 static const Entry* find_entry(const KernelKey& k) {
-    const Entry* tables[4] = {kShard0, kShard1, kShard2, kShard3};
-    const int sizes[4] = {kShard0Size, kShard1Size, kShard2Size, kShard3Size};
-    for (int t = 0; t < 4; ++t)
+    const Entry* tables[5] = {kShard0, kShard1, kShard2, kShard3, kShard4};
+    const int sizes[5] = {kShard0Size, kShard1Size, kShard2Size, kShard3Size, kShard4Size};
+    for (int t = 0; t < 5; ++t)
         for (int i = 0; i < sizes[t]; ++i) {
             const Entry& e = tables[t][i];
             if (e.key.kv == k.kv && e.key.scale == k.scale && e.key.vt == k.vt && e.key.head_dim == k.head_dim &&

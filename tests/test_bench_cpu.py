@@ -40,7 +40,8 @@ def test_kernel_tags_name_the_instances_rocprofv3_prints():
     assert bench.kernel_tag_of(I.BF16_P128) == "Cfg<0, 0, 0, 128, 128, 1, 0, 0, 0>"
     assert bench.kernel_tag_of(I.FP8TOK_Q1) == "Cfg<1, 2, 0, 256, 16, 1, 0, 0, 0>"
     assert bench.kernel_tag_of(I.FP8TOK_Q4) == "Cfg<1, 2, 0, 256, 16, 2, 0, 0, 0>"
-    assert bench.kernel_tag_of(I.FP8TOK_Q4_CAUSAL) == "Cfg<1, 2, 0, 256, 16, 2, 0, 0, 1>"
+    assert bench.kernel_tag_of(I.FP8TOK_Q4_CAUSAL) == "Cfg<1, 2, 0, 256, 16, 2, 0, 0, 2>"
+    assert bench.kernel_tag_of(I.BF16_P64_W1024) == "Cfg<0, 0, 0, 128, 64, 1, 0, 0, 1>"
     assert bench.kernel_tag_of(I.FP8_TRANS) == "Cfg<1, 1, 1, 128, 128, 1, 0, 0, 0>"
 
 

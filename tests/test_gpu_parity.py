@@ -261,6 +261,16 @@ GPU_MASK_SPECS = [
            window=600),
     I.Spec("g_fp8tok_d256_p128_q2_causal", 3, ("fixed", (1, 383, 1800)), 2, 1, 8, 256, 128, "fp8", "token",
            seed=49, causal=1),
+    # causal rows without a window on fp8 per-token caches (the causal-only
+    # instances): lengths whose earliest row ends in the tile before the last
+    # (L mod 256 in 1 .. qlen - 1), with 32 rows (two N tiles) at head_dim 256,
+    # 16 rows (one N tile, whole-stage prefetch), and transposed V
+    I.Spec("g_fp8tok_d256_p16_q4_causal_edges", 10, ("fixed", (1, 2, 3, 4, 257, 258, 259, 513, 1027, 767)), 4, 2,
+           8, 256, 16, "fp8", "token", seed=54, causal=1),
+    I.Spec("g_fp8tok_d256_p16_q2_causal_edges", 5, ("fixed", (1, 2, 257, 1025, 600)), 2, 1, 8, 256, 16, "fp8",
+           "token", seed=55, causal=1),
+    I.Spec("g_fp8tok_trans_d128_p64_q4_causal", 3, ("fixed", (3, 258, 700)), 4, 1, 4, 128, 64, "fp8", "token",
+           "trans", seed=56, causal=1),
     # fp8 per-token caches with 32 query rows at head_dim 256 on the V-by-DMA
     # path (query fragments in LDS): page 64 plain, page 128 causal + window
     I.Spec("g_fp8tok_d256_p64_q4", 3, ("fixed", (2, 900, 2100)), 4, 1, 8, 256, 64, "fp8", "token", seed=50),
