@@ -218,9 +218,11 @@ struct Cfg {
     // LDS DMA and is read back transposed; MXFP4 V is widened to bf16 in
     // registers and staged through LDS one 32-token PV step at a time.
     // Measured per configuration: one N tile (32 query rows only in the fp8
-    // per-token case below), and not for bf16 pages of 128 tokens (there the
-    // register path at one workgroup per CU beats the DMA path at one or two:
-    // 179.5 against 183-209 us on the batch-64 workload).
+    // per-token case below), and not for bf16 pages of 64 or 128 tokens without
+    // a window (there the register path at one workgroup per CU beats the DMA
+    // path at one or two on the batch-64 workload: 179.5 against 183-209 us at
+    // page 128, 174 against 184 us at page 64). The windowed bf16 page-64
+    // instance keeps the DMA path (window 1024: 51.8 against 55.2 us).
     //
     // The wait before PV allows the KVMEM loads issued after the slice's DMA to
     // be outstanding. Loads, the DMA included, complete in issue order, and any
@@ -241,7 +243,7 @@ struct Cfg {
     // live in LDS, leaving the registers to K, the scores and O.
     static constexpr bool NT4 = NT_ == 4;
     static constexpr bool VDMA = !VT && KV != KV_MXFP4 && (NT_ == 1 || NT2_DMA || NT4) &&
-                                 !(KV_ == KV_BF16 && PG_ == 128 && !NT4);
+                                 !(KV_ == KV_BF16 && !NT4 && (PG_ == 128 || (PG_ == 64 && WIN_ == 0)));
     static constexpr bool STAGE_V = !VT && !VDMA;
     // Register-staged V loads held at the top of the slice (see load_v): for
     // the fp8 per-token page-16 instance with 32 query rows at head_dim 256,
