@@ -254,7 +254,8 @@ def time_case(case, steps, warmup, flush, flush_out, extras=False, **problem_ove
     read leaves clean lines, where a write would leave dirty lines for the
     decode to write back); the median of the per-call event times is kept. The
     tile / merge split comes from the library's own events around each kernel,
-    in a separate pass of the same calls. With `extras`, also the differential
+    in a separate pass of the same cold calls; it is a mean, so a slow outlier
+    call shows there and not in the median. With `extras`, also the differential
     figure (see time_all) and the plan-free pa_decode_direct's cold median."""
     import statistics
 
@@ -286,6 +287,7 @@ def time_case(case, steps, warmup, flush, flush_out, extras=False, **problem_ove
     us = cold_median(call)
     plan.set_timing(True, steps)
     for _ in range(steps):
+        torch.amax(flush, dim=0, out=flush_out)  # same cold start as the median's calls
         call()
     torch.cuda.synchronize()
     t_ms, m_ms, n = plan.read_timing()
