@@ -270,6 +270,20 @@ struct Cfg {
     // at bf16 page 128 its smaller register count lets a second workgroup in,
     // which is slower there.
     static constexpr bool LAZY = PF;
+    // Whole-line K loads (load_k, fix_k) in the register-staged bf16
+    // instances with one N tile at head_dim 128: each load instruction reads
+    // whole 128-byte lines of 8 tokens, nontemporally, and one lane exchange
+    // per register then restores the MFMA operand layout. Measured on the
+    // batch-64 workload, us per call: 171.6 against 174.1 at page 64, 177.7
+    // against 180.0 at page 128. At head_dim 256 it measured 369 against 364
+    // us (page 64) and 354 against 355 (page 128), and in the fp8 per-token
+    // prefetch instance 70.1 against 70.3 (qlen 1): not used there.
+    static constexpr bool KLINE = KV_ == KV_BF16 && STAGE_V && NT_ == 1 && D_ == 128;
+    // These instances are held to one workgroup per compute unit by their LDS
+    // reservation (SMEM_ALLOC): at page 64 whole-line K frees the registers
+    // for a second one, which measured slower (a split plan and a merge:
+    // 180.9 against 174.6 us per call).
+    static constexpr bool ONE_PER_CU = KLINE;
     // query fragments in LDS (one copy per workgroup) instead of registers
     static constexpr bool QLDS = NT2_DMA || NT4;
     // register-staged V tile (bf16 rows): row pitch, extra offset per group of
@@ -287,6 +301,8 @@ struct Cfg {
     static constexpr int OPITCH = D + 4;                             // floats
     static constexpr int EPI_BYTES = 2 * ROWS_PAD * OPITCH * 4 + 2 * 4 * ROWS_PAD * 4;
     static constexpr int SMEM = (4 * WAVE_LDS + QLDS_BYTES > EPI_BYTES) ? 4 * WAVE_LDS + QLDS_BYTES : EPI_BYTES;
+    static constexpr int kLdsPerCu = 160 * 1024;
+    static constexpr int SMEM_ALLOC = ONE_PER_CU && SMEM <= kLdsPerCu / 2 ? kLdsPerCu / 2 + 256 : SMEM;
     // staging geometry for token-major V loads
     static constexpr int LPR = ROWB / 16;         // lanes per token row
     static constexpr int TPI = 64 / LPR;          // tokens per load instruction
@@ -585,15 +601,32 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
     constexpr int PG = C::PG;
     const int ln = cx.ln, lg = cx.lg;
     const int ktok0 = 16 * (ln >> 2) + (ln & 3);
-    const char* krow = cx.kbase + (long)sp.kpage * a.num_kv_heads * C::PAGE_BYTES_HEAD +
-                       (long)slot_in_page(sp, ktok0) * C::ROWB;
+    if constexpr (C::KLINE) {
+        // Lanes ln = 2p and 2p + 1 read the two 64-byte halves of one line:
+        // call (c, 2L) line L of token t(2p) = 16*(ln>>2) + (ln&2) + 4c, call
+        // (c, 2L + 1) line L of token t(2p) + 1 (same page). Each call then
+        // covers line L of 8 whole token rows; fix_k exchanges the halves.
+        const char* krow = cx.kbase + (long)sp.kpage * a.num_kv_heads * C::PAGE_BYTES_HEAD +
+                           (long)slot_in_page(sp, ktok0 & ~1) * C::ROWB + 64 * (ln & 1) + 16 * lg;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int u = 0; u < C::KLOADS; ++u) {
-            const char* src = krow + 4 * c * C::ROWB + 64 * u + 16 * lg;
-            kb.k[c][u] = C::ROWB <= 64 ? ld16_kv(src) : ld16(src);
-        }
+            for (int L = 0; L < C::KLOADS / 2; ++L) {
+                const char* src = krow + 4 * c * C::ROWB + 128 * L;
+                kb.k[c][2 * L] = ld16_kv(src);
+                kb.k[c][2 * L + 1] = ld16_kv(src + C::ROWB);
+            }
+    } else {
+        const char* krow = cx.kbase + (long)sp.kpage * a.num_kv_heads * C::PAGE_BYTES_HEAD +
+                           (long)slot_in_page(sp, ktok0) * C::ROWB;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int u = 0; u < C::KLOADS; ++u) {
+                const char* src = krow + 4 * c * C::ROWB + 64 * u + 16 * lg;
+                kb.k[c][u] = C::ROWB <= 64 ? ld16_kv(src) : ld16(src);
+            }
+    }
     if constexpr (C::KV == KV_MXFP4) {
         const char* srow = cx.ksbase + (long)sp.kpage * a.num_kv_heads * PG * C::SROWB +
                            (long)slot_in_page(sp, ktok0) * C::SROWB;
@@ -614,6 +647,35 @@ PA_DEV void load_k(const TileArgs& a, const Ctx& cx, const SlicePages<C>& sp, KB
                 kb.tvs[4 * i + j] = __builtin_bit_cast(float, vw);
             }
         }
+    }
+}
+
+// Whole-line K loads, once landed: lane 2p holds the low halves (bytes
+// 128L + [0, 64) of a row) of tokens t(2p) and t(2p) + 1, lane 2p + 1 the high
+// halves of the same two tokens. Exchanging the second register of the even
+// lane with the first of the odd lane leaves each lane with its own token's
+// bytes, as the MFMA operand layout of KBuf::k expects. The partner lane
+// (ln ^ 1) is read with the DPP quad permutation [1, 0, 3, 2].
+template <class C>
+PA_DEV void fix_k(const Ctx& cx, KBuf<C>& kb) {
+    if constexpr (C::KLINE) {
+        constexpr int kSwapPairs = 0xB1;  // quad_perm [1, 0, 3, 2]: lane ^ 1
+        const bool odd = cx.ln & 1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int L = 0; L < C::KLOADS / 2; ++L) {
+                u32x4& lo = kb.k[c][2 * L];
+                u32x4& hi = kb.k[c][2 * L + 1];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t x = lo[j], y = hi[j];
+                    const uint32_t px = __builtin_amdgcn_mov_dpp((int)x, kSwapPairs, 0xF, 0xF, true);
+                    const uint32_t py = __builtin_amdgcn_mov_dpp((int)y, kSwapPairs, 0xF, 0xF, true);
+                    lo[j] = odd ? py : x;
+                    hi[j] = odd ? y : px;
+                }
+            }
     }
 }
 
@@ -1324,7 +1386,7 @@ PA_DEV void finish_task(const TileArgs& a, const Ctx& cx, State<C>& st, int part
 
 template <class C>
 __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const TileArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM_ALLOC];
 
     Ctx cx;
     cx.lane = threadIdx.x & 63;
@@ -1439,6 +1501,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
             dma_fence<C>();
             load_v<C>(a, cx, sp, vb, vlds);
             PFrag<C> pf;
+            fix_k<C>(cx, kb);
             qk_softmax<C, M>(a, cx, qf, kb, st, pf, cb, qlds);
             sp = slice_pages<C>(a, cx, pc, tile + 1);
             load_k<C>(a, cx, sp, kb);
@@ -1454,6 +1517,7 @@ __global__ __launch_bounds__(kTileThreads, C::MINB) void pa_tile_kernel(const Ti
         dma_fence<C>();
         load_v<C>(a, cx, sp, vb, vlds);
         PFrag<C> pf;
+        fix_k<C>(cx, kb);
         qk_softmax<C, true>(a, cx, qf, kb, st, pf, cb, qlds);
         pv<C, true, 0>(cx, vb, pf, st, cb, vlds);
     }
