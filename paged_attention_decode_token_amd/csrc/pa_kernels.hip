@@ -270,20 +270,26 @@ struct Cfg {
     // at bf16 page 128 its smaller register count lets a second workgroup in,
     // which is slower there.
     static constexpr bool LAZY = PF;
-    // Whole-line K loads (load_k, fix_k) in the register-staged bf16
-    // instances with one N tile at head_dim 128: each load instruction reads
-    // whole 128-byte lines of 8 tokens, nontemporally, and one lane exchange
-    // per register then restores the MFMA operand layout. Measured on the
-    // batch-64 workload, us per call: 171.6 against 174.1 at page 64, 177.7
-    // against 180.0 at page 128. At head_dim 256 it measured 369 against 364
-    // us (page 64) and 354 against 355 (page 128), and in the fp8 per-token
-    // prefetch instance 70.1 against 70.3 (qlen 1): not used there.
-    static constexpr bool KLINE = KV_ == KV_BF16 && STAGE_V && NT_ == 1 && D_ == 128;
-    // These instances are held to one workgroup per compute unit by their LDS
-    // reservation (SMEM_ALLOC): at page 64 whole-line K frees the registers
-    // for a second one, which measured slower (a split plan and a merge:
-    // 180.9 against 174.6 us per call).
-    static constexpr bool ONE_PER_CU = KLINE;
+    // Whole-line K loads (load_k, fix_k) at head_dim 128 with one N tile, in
+    // the bf16 instances and the fp8 per-tensor transposed-V ones (with
+    // per-token scales those already spill at three workgroups per CU, and
+    // whole-line K adds to it): each load instruction
+    // reads whole 128-byte lines of 8 tokens, nontemporally, and one lane
+    // exchange per register then restores the MFMA operand layout. Measured
+    // cold per call, us: bf16 batch 64, 171.6 against 174.1 at page 64 and
+    // 177.7 against 180.0 at page 128, 50.2 against 52.0 with a 1024-token
+    // window (V by DMA); fp8 transposed V, batch 256 x 16384, 165.0 against
+    // 182.6. Not used where it measured no faster: head_dim 256 (bf16, 369
+    // against 364 at page 64), the fp8 per-token prefetch instance (70.1
+    // against 70.3, qlen 1) and its 32-row instances (75.9 against 76.1 at
+    // qlen 4, 68.7 against 68.4 with causal rows).
+    static constexpr bool KLINE = NT_ == 1 && D_ == 128 && (KV_ == KV_BF16 || (KV_ == KV_FP8 && VT_ && SC_ != SC_TOKEN));
+    // The register-staged bf16 ones are held to one workgroup per compute
+    // unit by their LDS reservation (SMEM_ALLOC): at page 64 whole-line K
+    // frees the registers for a second one, which measured slower (a split
+    // plan and a merge: 180.9 against 174.6 us per call).
+    static constexpr bool ONE_PER_CU = KLINE && KV_ == KV_BF16 && STAGE_V;
+    static_assert(!(KLINE && PF), "fix_k runs in the loop without the whole-stage prefetch only");
     // query fragments in LDS (one copy per workgroup) instead of registers
     static constexpr bool QLDS = NT2_DMA || NT4;
     // register-staged V tile (bf16 rows): row pitch, extra offset per group of
