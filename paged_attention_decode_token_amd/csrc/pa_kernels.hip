@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -1551,6 +1553,9 @@ PA_DEV float wave_sum(float v) {
 // out = sum_p w_p O_p / sum_p w_p l_p, summed in partition order (PR #7056,
 // "Bandwidth": the partition reducer). Lane p reads partition p's (m, l); the
 // weighted sum of the O_p rows then runs over p with D/64 elements per lane.
+// The O rows of the first kMergePre partitions are loaded together with the
+// (m, l) pairs, since they depend only on the partition table: the kernel then
+// waits on memory twice (table, then partials) rather than three times.
 template <int D>
 __global__ __launch_bounds__(256) void pa_merge_kernel(const TileArgs a) {
     const int lane = threadIdx.x & 63;
@@ -1564,11 +1569,23 @@ __global__ __launch_bounds__(256) void pa_merge_kernel(const TileArgs a) {
     const int kvh = h / a.q_per_kv;
     const int r = i * a.q_per_kv + h % a.q_per_kv;
     const int pair = b * a.num_kv_heads + kvh;
-    const int P = a.plan_free ? a.uniform_parts : a.seq_parts[2 * pair];
+    // the row's (sequence, KV head) is the same for the whole wave
+    const int P = uniform(a.plan_free ? a.uniform_parts : a.seq_parts[2 * pair]);
     if (P <= 1) return;
-    const long unit0 = a.plan_free ? (long)pair * P : a.seq_parts[2 * pair + 1];
+    const long unit0 = uniform(a.plan_free ? pair * P : a.seq_parts[2 * pair + 1]);
     const long stride = a.rows;  // rows between consecutive partitions
     const long prow0 = unit0 * a.rows + r;
+    constexpr int PER = D / 64;
+    constexpr int kMergePre = 16;
+    const float* po = a.part_o + prow0 * D + PER * lane;
+    using Row = typename std::conditional<PER == 4, f32x4, f32x2>::type;  // this lane's PER elements
+    static_assert(PER == 2 || PER == 4, "head_dim 128 or 256");
+    Row pre[kMergePre];
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u) {
+        pre[u] = Row{};
+        if (u < P) pre[u] = *reinterpret_cast<const Row*>(po + u * stride * D);
+    }
     float m = -__builtin_inff(), l = 0.f;
     if (lane < P) {
         const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * (prow0 + lane * stride));
@@ -1578,12 +1595,18 @@ __global__ __launch_bounds__(256) void pa_merge_kernel(const TileArgs a) {
     const float M = wave_max(m);
     const float w = (lane < P && M != -__builtin_inff()) ? fast_exp2(m - M) : 0.f;
     const float den = wave_sum(w * l);
-    constexpr int PER = D / 64;
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    const float* po = a.part_o + prow0 * D + PER * lane;
-    int p = 0;
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u) {
+        if (u < P) {
+            const float wp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+#pragma unroll
+            for (int k = 0; k < PER; ++k) acc[k] += wp * pre[u][k];
+        }
+    }
+    int p = kMergePre;
     for (; p + 4 <= P; p += 4) {
         float v[4][PER];
 #pragma unroll
