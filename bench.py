@@ -364,7 +364,7 @@ def time_per_config(steps, warmup):
     return rows
 
 
-def time_all(steps, warmup, names=None):
+def time_all(steps, warmup, names=None, task_budgets=(0,)):
     """Per workload: cold-cache median us per pa_decode call, and the tile / merge
     kernel split from the library's events (inputs resident in HBM).
 
@@ -372,7 +372,9 @@ def time_all(steps, warmup, names=None):
     which is a tenth of a 60 us call). So a second, differential figure is taken
     too: `steps` cold calls (flush, call, flush, call, ...) between two events,
     minus `steps` flushes alone between two events, divided by `steps` (median
-    of five alternating pairs of batches)."""
+    of five alternating pairs of batches). With several task budgets (0: the
+    planner's automatic choice) each workload is timed once per budget, and
+    the rows of budgets other than 0 are keyed `name@budget`."""
     import torch
 
     from paged_attention_decode_token_amd import inputs as I
@@ -383,13 +385,16 @@ def time_all(steps, warmup, names=None):
     specs = I.FULL if not names else [I.BY_NAME[n] for n in names]
     for spec in specs:
         case = I.make_case(spec)
-        row = time_case(case, steps, warmup, flush, flush_out, extras=True)
-        rows[spec.name] = row
-        print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  differential %8.2f us %5.1f%%  tile %8.2f us  tasks %5d slots %4d  "
-              "plan-free %8.2f us" % (spec.name, row["us_per_call"], row["kv_GBps"], row["pct_of_hbm_peak"],
-                                      row["us_per_call_differential"], row["pct_of_hbm_peak_differential"],
-                                      row["tile_us"], row["tasks"], row["slots"], row["plan_free_us_per_call"]),
-              file=sys.stderr, flush=True)
+        for budget in task_budgets:
+            row = time_case(case, steps, warmup, flush, flush_out, extras=True, task_budget=budget)
+            key = spec.name if budget == 0 else "%s@%d" % (spec.name, budget)
+            rows[key] = row
+            print("%-32s %9.2f us  %7.1f GB/s  %5.1f%%  differential %8.2f us %5.1f%%  tile %8.2f us  merge %6.2f us  "
+                  "tasks %5d slots %4d  plan-free %8.2f us" % (
+                      key, row["us_per_call"], row["kv_GBps"], row["pct_of_hbm_peak"],
+                      row["us_per_call_differential"], row["pct_of_hbm_peak_differential"], row["tile_us"],
+                      row["merge_us"], row["tasks"], row["slots"], row["plan_free_us_per_call"]),
+                  file=sys.stderr, flush=True)
         del case
     return rows
 
@@ -511,6 +516,9 @@ def main():
                     help="also time the MXFP4 paged MQA-logits workloads (implied by --all)")
     ap.add_argument("--workloads", default="",
                     help="with --all: comma-separated workload names to time (default: every workload)")
+    ap.add_argument("--task-budgets", default="0",
+                    help="with --all: comma-separated task budgets to plan each workload with "
+                         "(0: the planner's automatic choice)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -627,7 +635,8 @@ def main():
         res["per_config"] = time_per_config(args.steps, args.warmup)
     if args.all:
         res["all_workloads"] = time_all(args.steps, args.warmup,
-                                        [w for w in args.workloads.split(",") if w] or None)
+                                        [w for w in args.workloads.split(",") if w] or None,
+                                        [int(b) for b in args.task_budgets.split(",") if b] or [0])
     if args.all or args.kv_write:
         res["kv_write"] = time_writes(args.steps, args.warmup)
     if args.all or args.mqa:
