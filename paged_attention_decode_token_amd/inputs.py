@@ -156,7 +156,15 @@ FP8TOK_Q4_CAUSAL = FP8TOK_Q4.replace(name="fp8tok_p16_b16_q4_causal", causal=1, 
 
 FULL = [TINY_BF16, BF16_P64, BF16_P128, FP8TOK_Q1, FP8TOK_Q4, FP8_TRANS, MXFP4_SHORT_Q8, MXFP4_SHORT_QBF,
         MXFP4_LONG_Q8, MXFP4_LONG_QBF, BF16_P64_W1024, FP8TOK_Q4_CAUSAL]
-BY_NAME = {s.name: s for s in FULL}
+# The kernel-performance shapes of the NaN-safe V mask page (ROCm/aiter PR #7092, "All 513 shapes")
+# for fp8 per-token page-16 caches, 2 KV heads x GQA 8, head_dim 256, batch 16: every sequence holds
+# ctx - U[0, 255] tokens. Timed by `bench.py --all --workloads ...` only; not parity batches.
+FP8TOK_Q1_C16K = FP8TOK_Q1.replace(name="fp8tok_p16_b16_q1_c16384", lens=("uniform", 16129, 16384), seed=1030)
+FP8TOK_Q4_C16K = FP8TOK_Q4.replace(name="fp8tok_p16_b16_q4_c16384", lens=("uniform", 16129, 16384), seed=1031)
+FP8TOK_Q1_C64K = FP8TOK_Q1.replace(name="fp8tok_p16_b16_q1_c65536", lens=("uniform", 65281, 65536), seed=1032)
+FP8TOK_Q4_C64K = FP8TOK_Q4.replace(name="fp8tok_p16_b16_q4_c65536", lens=("uniform", 65281, 65536), seed=1033)
+PAGE_SHAPES = [FP8TOK_Q1_C16K, FP8TOK_Q4_C16K, FP8TOK_Q1_C64K, FP8TOK_Q4_C64K]
+BY_NAME = {s.name: s for s in FULL + PAGE_SHAPES}
 
 
 def small(spec: Spec) -> Spec:
