@@ -163,7 +163,20 @@ FP8TOK_Q1_C16K = FP8TOK_Q1.replace(name="fp8tok_p16_b16_q1_c16384", lens=("unifo
 FP8TOK_Q4_C16K = FP8TOK_Q4.replace(name="fp8tok_p16_b16_q4_c16384", lens=("uniform", 16129, 16384), seed=1031)
 FP8TOK_Q1_C64K = FP8TOK_Q1.replace(name="fp8tok_p16_b16_q1_c65536", lens=("uniform", 65281, 65536), seed=1032)
 FP8TOK_Q4_C64K = FP8TOK_Q4.replace(name="fp8tok_p16_b16_q4_c65536", lens=("uniform", 65281, 65536), seed=1033)
-PAGE_SHAPES = [FP8TOK_Q1_C16K, FP8TOK_Q4_C16K, FP8TOK_Q1_C64K, FP8TOK_Q4_C64K]
+# the same page's bf16 and fp8 per-tensor shapes (2 KV heads x GQA 8, head_dim 256, qlen 1)
+BF16_D256_P64_C4K = _spec("bf16_d256_p64_b64_c4096", num_seqs=64, lens=("uniform", 3841, 4096), qlen=1,
+                          num_kv_heads=2, q_per_kv=8, head_dim=256, page_size=64, kv_dtype="bf16", fill="inf",
+                          seed=1034)
+BF16_D256_P128_C4K = BF16_D256_P64_C4K.replace(name="bf16_d256_p128_b64_c4096", page_size=128, seed=1035)
+BF16_D256_P64_C16K = BF16_D256_P64_C4K.replace(name="bf16_d256_p64_b64_c16384", lens=("uniform", 16129, 16384),
+                                               seed=1036)
+BF16_D256_P128_C16K = BF16_D256_P64_C16K.replace(name="bf16_d256_p128_b64_c16384", page_size=128, seed=1037)
+FP8_D256_P128_B64_C16K = BF16_D256_P128_C16K.replace(name="fp8_d256_p128_b64_c16384", kv_dtype="fp8",
+                                                     scale_mode="tensor", fill="nan", seed=1038)
+FP8_D256_P128_B256_C16K = FP8_D256_P128_B64_C16K.replace(name="fp8_d256_p128_b256_c16384", num_seqs=256,
+                                                         seed=1039)
+PAGE_SHAPES = [FP8TOK_Q1_C16K, FP8TOK_Q4_C16K, FP8TOK_Q1_C64K, FP8TOK_Q4_C64K, BF16_D256_P64_C4K, BF16_D256_P128_C4K,
+               BF16_D256_P64_C16K, BF16_D256_P128_C16K, FP8_D256_P128_B64_C16K, FP8_D256_P128_B256_C16K]
 BY_NAME = {s.name: s for s in FULL + PAGE_SHAPES}
 
 
