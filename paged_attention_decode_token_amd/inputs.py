@@ -175,8 +175,11 @@ FP8_D256_P128_B64_C16K = BF16_D256_P128_C16K.replace(name="fp8_d256_p128_b64_c16
                                                      scale_mode="tensor", fill="nan", seed=1038)
 FP8_D256_P128_B256_C16K = FP8_D256_P128_B64_C16K.replace(name="fp8_d256_p128_b256_c16384", num_seqs=256,
                                                          seed=1039)
+BF16_D256_P16_B1_C1K = BF16_D256_P64_C4K.replace(name="bf16_d256_p16_b1_c1024", num_seqs=1, lens=("uniform", 769, 1024),
+                                                 page_size=16, seed=1040)
 PAGE_SHAPES = [FP8TOK_Q1_C16K, FP8TOK_Q4_C16K, FP8TOK_Q1_C64K, FP8TOK_Q4_C64K, BF16_D256_P64_C4K, BF16_D256_P128_C4K,
-               BF16_D256_P64_C16K, BF16_D256_P128_C16K, FP8_D256_P128_B64_C16K, FP8_D256_P128_B256_C16K]
+               BF16_D256_P64_C16K, BF16_D256_P128_C16K, FP8_D256_P128_B64_C16K, FP8_D256_P128_B256_C16K,
+               BF16_D256_P16_B1_C1K]
 BY_NAME = {s.name: s for s in FULL + PAGE_SHAPES}
 
 
