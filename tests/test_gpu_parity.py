@@ -368,3 +368,32 @@ def test_window_plan_with_shorter_device_lengths(spec):
             out, _ = B.decode_case(short, plan=plan)
             torch.cuda.synchronize()
             check_parity(out, ref, what="%s cut %d %s" % (spec.name, cut, over))
+
+
+# Transposed V ([D][page] per page and head) with one N tile at head_dim 128, at every page size, for
+# bf16 and fp8 per-tensor caches: the instances whose K goes by whole-line loads and a lane exchange
+# (and, at page 128 fp8, the transposed-V workload's). Ragged lengths with partial first and last
+# pages, planned (automatic and one tile per task), plan-free, and with poisoned unowned rows.
+VT_SPECS = [
+    I.Spec("g_%s_trans_p%d" % (kv, pg), 6, ("fixed", (1, 17, 63, 300, 777, 1300)), 1, 2, 8, 128, pg, kv,
+           "tensor" if kv == "fp8" else "none", "trans", seed=70 + 3 * i + j)
+    for i, kv in enumerate(("bf16", "fp8")) for j, pg in enumerate((16, 64, 128))
+] + [
+    I.Spec("g_%s_trans_p%d_q2_causal" % (kv, pg), 4, ("fixed", (2, 65, 700, 1025)), 2, 1, 8, 128, pg, kv,
+           "tensor" if kv == "fp8" else "none", "trans", seed=80 + j, causal=1)
+    for j, (kv, pg) in enumerate((("bf16", 16), ("fp8", 64)))
+]
+
+
+@pytest.mark.parametrize("spec", VT_SPECS, ids=lambda s: s.name)
+def test_transposed_v_page_sizes(spec):
+    case = I.make_case(spec)
+    ref = oracle.pa_decode(case)
+    for over in ({}, {"task_budget": 100000}):
+        out, _ = run(case, **over)
+        check_parity(out, ref, what="%s %s" % (spec.name, over))
+    check_parity(run_direct(case), ref, what="%s plan-free" % spec.name)
+    zero = I.make_case(spec, fill="zero")
+    ref_bits = _bits(run(zero)[0])
+    for fill in ("nan", "random"):
+        assert np.array_equal(_bits(run(I.refill(zero, fill))[0]), ref_bits), "%s: %s fill" % (spec.name, fill)
