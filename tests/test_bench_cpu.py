@@ -54,3 +54,22 @@ def test_traffic_is_keyed_to_the_kernel_source():
         assert tr == doc["kernels"]["bf16_p64_b64"]["hbm_bytes_per_launch"]
     else:
         assert tr is None
+
+
+def test_page_shapes_are_bench_only_and_follow_the_pages_recipe():
+    # timed by `bench.py --all --workloads`, not part of the parity batches
+    full = {s.name for s in I.FULL}
+    for s in I.PAGE_SHAPES:
+        assert s.name not in full and I.BY_NAME[s.name] is s
+        assert (s.num_kv_heads, s.q_per_kv, s.head_dim) == (2, 8, 256)
+        kind, lo, hi = s.lens
+        # ctx - U[0, 255] tokens per sequence
+        assert kind == "uniform" and hi - lo == 255 and hi & (hi - 1) == 0
+    tags = {bench.kernel_tag_of(s) for s in I.PAGE_SHAPES}
+    assert "Cfg<1, 2, 0, 256, 16, 1, 0, 0, 0>" in tags and "Cfg<1, 1, 0, 256, 128, 1, 0, 0, 0>" in tags
+
+
+def test_task_budgets_option_is_parsed_for_the_all_table():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0 and "--task-budgets" in r.stdout
