@@ -583,6 +583,12 @@ PA_DEV void page_cache_fill(const TileArgs& a, const Ctx& cx, PageCache<C>& pc, 
     const int tile = tile0 + cx.lane / C::NPC;
     const int slot = (tile * kTileTokens + 64 * cx.wave) / C::PG + cx.lane % C::NPC;
     pc.pgv = page_of<C, true>(a, cx, slot);
+    // With pages longer than a slice, a slice that starts at or past L can lie
+    // in the last owned page: it reads block 0 as well (the same rows for every
+    // task, so mostly from L2) instead of the page's unowned rows from HBM. The
+    // last tile's masks discard its scores and zero its V either way.
+    if constexpr (C::PG > 64)
+        if (tile * kTileTokens + 64 * cx.wave >= cx.L) pc.pgv = 0;
 }
 
 PA_DEV int lane_value(int v, int src_lane) { return __builtin_amdgcn_ds_bpermute(src_lane << 2, v); }
