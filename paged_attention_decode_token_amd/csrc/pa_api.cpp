@@ -311,16 +311,38 @@ pa_status build_plan(const pa_problem& p, const int32_t* lens, int num_cus, int 
                 }
             }
         }
-        // longest first; ties keep (sequence, head, partition) order
+        // longest first; ties in (sequence, partition, head) order, so that the
+        // KV heads of one partition are neighbours
         const size_t n = out->tasks.size() / 4;
+        const auto& t = out->tasks;
         std::vector<size_t> order(n);
         std::iota(order.begin(), order.end(), 0);
-        std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) {
-            return out->tasks[4 * x + 3] - out->tasks[4 * x + 2] > out->tasks[4 * y + 3] - out->tasks[4 * y + 2];
+        std::sort(order.begin(), order.end(), [&](size_t x, size_t y) {
+            const int32_t sx = t[4 * x + 3] - t[4 * x + 2], sy = t[4 * y + 3] - t[4 * y + 2];
+            if (sx != sy) return sx > sy;
+            if (t[4 * x] != t[4 * y]) return t[4 * x] < t[4 * y];
+            const int32_t px = t[4 * x + 1] >> 16, py = t[4 * y + 1] >> 16;
+            if (px != py) return px < py;
+            return (t[4 * x + 1] & 0xFFFF) < (t[4 * y + 1] & 0xFFFF);
         });
+        // Per-token scales of 16-token pages: the scale rows of KV heads 2k and
+        // 2k + 1 of a page share one 128-byte line ([block][head][16] fp32). The
+        // two heads' tasks of a partition (neighbours above, same length) are
+        // placed 8 launch slots apart, which the hardware dispatches to the same
+        // XCD, so the line comes from HBM once and the second read finds it in
+        // that XCD's L2. Within each run of 16 tasks, slot 16m + 8s + x takes
+        // task 2 (8m + x) + s; the runs stay in longest-first order.
+        const bool pair_heads = p.scale_mode == PA_SCALE_PER_TOKEN && p.page_size * 4 < 128 && H % 2 == 0;
+        std::vector<size_t> slot_task(n);
+        for (size_t i = 0; i < n; ++i) slot_task[i] = i;
+        if (pair_heads)
+            for (size_t i = 0; i < n / 16 * 16; ++i) {
+                const size_t m = i / 16, s8 = (i / 8) % 2, x = i % 8;
+                slot_task[i] = 2 * (8 * m + x) + s8;
+            }
         std::vector<int32_t> sorted(out->tasks.size());
         for (size_t i = 0; i < n; ++i)
-            for (int k = 0; k < 4; ++k) sorted[4 * i + k] = out->tasks[4 * order[i] + k];
+            for (int k = 0; k < 4; ++k) sorted[4 * i + k] = t[4 * order[slot_task[i]] + k];
         out->tasks.swap(sorted);
     }
     const size_t n = out->tasks.size() / 4;

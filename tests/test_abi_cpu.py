@@ -4,6 +4,7 @@ owned tile exactly once. No GPU is touched."""
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -229,6 +230,41 @@ def test_planner_covers_every_owned_tile_once(lens, budget, maxp):
     if maxp:
         assert int(parts[:, 0].max()) <= maxp
     assert info.num_tasks == len(tasks)
+
+
+@pytest.mark.parametrize("heads,pages", [(2, 16), (4, 16), (2, 64), (3, 16)])
+def test_planner_pairs_heads_that_share_scale_lines(heads, pages):
+    # fp8 with per-token scales: at 16-token pages the scale rows of heads 2k and 2k + 1 of a
+    # page share a 128-byte line, and their tasks go 8 launch slots apart (one XCD)
+    rng = np.random.default_rng(7)
+    lens = rng.integers(2048, 32769, size=16).tolist()
+    p = _prob(num_seqs=16, num_kv_heads=heads, head_dim=256, page_size=pages, kv_dtype=B.PA_KV_FP8_E4M3,
+              scale_mode=B.PA_SCALE_PER_TOKEN, max_blocks_per_seq=32768 // pages, num_blocks=20000,
+              max_context_len=32768)
+    tasks, parts, info = B.pa_plan_host(p, lens, num_cus=256, blocks_per_cu=1)
+    rows = tasks.tolist()
+    # every owned tile exactly once
+    seen = set()
+    for b, kp, t0, t1 in rows:
+        for t in range(t0, t1):
+            assert (b, kp & 0xFFFF, t) not in seen
+            seen.add((b, kp & 0xFFFF, t))
+    assert seen == {(b, h, t) for b, L in enumerate(lens) for h in range(heads) for t in range((L + 255) // 256)}
+    sizes = [t1 - t0 for _, _, t0, t1 in rows]
+    n = len(rows)
+    if pages == 16 and heads % 2 == 0:
+        full = n // 16 * 16
+        for m in range(0, full, 16):
+            for x in range(8):
+                a, c = rows[m + x], rows[m + 8 + x]
+                assert a[0] == c[0] and a[2:] == c[2:] and (a[1] >> 16) == (c[1] >> 16)
+                assert (a[1] & 0xFFFF) % 2 == 0 and (c[1] & 0xFFFF) == (a[1] & 0xFFFF) + 1
+        runs = [sizes[m:m + 16] for m in range(0, full, 16)] + [[s] for s in sizes[full:]]
+        for r0, r1 in zip(runs, runs[1:]):
+            assert min(r0) >= max(r1)
+        assert sizes[full:] == sorted(sizes[full:], reverse=True)
+    else:
+        assert sizes == sorted(sizes, reverse=True)
 
 
 def test_planner_without_host_lengths_uses_max_context():
