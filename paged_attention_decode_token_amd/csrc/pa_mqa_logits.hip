@@ -29,9 +29,10 @@
 // HBM-bound: per (row, position) one K row (64 data + 4 scale bytes) is read
 // and one fp32 score written; the row's q, scales and weights (4.4 KB at 64
 // heads) are read once per workgroup and stay in L2. K data is loaded and the
-// scores stored nontemporally (16 rows x 131072 positions, 64 heads, cold:
-// 39.6 -> 38.2 us per call; two rows per sequence over 32768 positions, whose
-// rows share K in one L2, 21.6 -> 21.7 us).
+// scores stored nontemporally, the scores as whole lines (16 rows x 131072
+// positions, 64 heads, cold: 39.7 -> 37.3 us per call; two rows per sequence
+// over 32768 positions 21.7 -> 20.9 us). Nontemporal stores of 64-byte pieces
+// did not merge in L2 and wrote 1.26x the score bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
