@@ -814,8 +814,9 @@ pa_status pa_mqa_logits_mxfp4(const pa_mqa_problem* problem, const void* q, cons
         return fail(PA_ERR_UNSUPPORTED, "a table, pool or output row beyond 2^31 positions");
     const long long max_pos = std::min(reach, (long long)p.out_stride);
     const long long chunks = (max_pos + pa::kMqChunkPositions - 1) / pa::kMqChunkPositions;
-    if ((long long)p.num_rows * chunks >= (1LL << 31))
-        return fail(PA_ERR_UNSUPPORTED, "num_rows * ceil(positions / %d) exceeds 2^31", pa::kMqChunkPositions);
+    // one workgroup per (chunk, row), the grid rounded up to a multiple of 8
+    if ((long long)p.num_rows * chunks > (1LL << 31) - 8)
+        return fail(PA_ERR_UNSUPPORTED, "num_rows * ceil(positions / %d) exceeds 2^31 - 8", pa::kMqChunkPositions);
     if (p.num_rows == 0 || max_pos == 0) return PA_OK;
     if (!q || !q_scale || !weights || !k_cache || !k_scale || !block_tables || !row_to_batch || !local_starts ||
         !local_ends || !out)

@@ -12,9 +12,10 @@
 // Built with the MFMA results in ordinary VGPRs (-amdgpu-mfma-vgpr-form): the
 // accumulator-register form costs one copy per result element here.
 //
-// Work: a workgroup takes 512 positions of one row; each wave 128 of them as
-// eight 16-token tiles (longer waves, double-buffered or not, measured slower:
-// what pays is many waves with their loads in flight). Per tile and group of
+// Work: a workgroup is one wave, which takes 128 positions of one row as eight
+// 16-token tiles (longer waves, double-buffered or not, measured slower: what
+// pays is many waves with their loads in flight; workgroups of one wave beat
+// four, 37.2 -> 36.3 us cold on the 16 x 131072 decode, and eight, 38.5 us). Per tile and group of
 // 16 heads, one
 // v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 on both sides gives
 // S[head][token]: A = the row's q (16 heads, loaded once per wave), B = the
@@ -28,7 +29,7 @@
 //
 // HBM-bound: per (row, position) one K row (64 data + 4 scale bytes) is read
 // and one fp32 score written; the row's q, scales and weights (4.4 KB at 64
-// heads) are read once per workgroup and stay in L2. K data is loaded and the
+// heads) are read once per wave and stay in L2. K data is loaded and the
 // scores stored nontemporally, the scores as whole lines (16 rows x 131072
 // positions, 64 heads, cold: 39.7 -> 37.3 us per call; two rows per sequence
 // over 32768 positions 21.7 -> 20.9 us). Nontemporal stores of 64-byte pieces
@@ -49,7 +50,8 @@ typedef uint32_t mq_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMqTiles = 8;              // 16-token tiles per wave
 constexpr int kMqWave = 16 * kMqTiles;   // positions per wave
-constexpr int kMqChunk = 4 * kMqWave;    // positions per workgroup (four waves)
+constexpr int kMqWaves = 1;              // waves per workgroup
+constexpr int kMqChunk = kMqWaves * kMqWave;  // positions per workgroup
 static_assert(kMqChunk == kMqChunkPositions, "the host sizes the grid by kMqChunkPositions");
 constexpr uint32_t kMqXcds = 8;  // accelerator complex dies of an MI355X
 
@@ -68,7 +70,7 @@ MQ_DEV float mq_relu(float x) {
 // once (one per lane) and hands each tile its page id by a lane shuffle, then
 // issues every tile's K load before the first MFMA, so no load waits on another.
 template <int HT>
-__global__ __launch_bounds__(256) void pa_mqa_logits_mxfp4_kernel(const MqaArgs a) {
+__global__ __launch_bounds__(64 * kMqWaves) void pa_mqa_logits_mxfp4_kernel(const MqaArgs a) {
     // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
     // contiguous range of (chunk, row) work items, rows fastest, so the rows
     // that share a chunk's K rows meet in one L2. The grid is a multiple of 8.
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(256) void pa_mqa_logits_mxfp4_kernel(const MqaArgs 
 template <int HT>
 hipError_t launch_h(const MqaArgs& a, hipStream_t stream) {
     const uint32_t grid = (a.items + kMqXcds - 1) / kMqXcds * kMqXcds;
-    hipLaunchKernelGGL((pa_mqa_logits_mxfp4_kernel<HT>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((pa_mqa_logits_mxfp4_kernel<HT>), dim3(grid), dim3(64 * kMqWaves), 0, stream, a);
     return hipGetLastError();
 }
 
