@@ -67,7 +67,7 @@ hipError_t launch_kv_write_mxfp4(int head_dim, const KvWriteArgs& args, hipStrea
 
 // MXFP4 paged MQA logits (head_dim 128): one workgroup per (chunk of
 // kMqChunkPositions positions, row) work item.
-constexpr int kMqChunkPositions = 128;
+constexpr int kMqChunkPositions = 192;
 struct MqaArgs {
     const uint8_t* q;        // [rows][H][64]
     const uint8_t* q_scale;  // [rows][H][4]

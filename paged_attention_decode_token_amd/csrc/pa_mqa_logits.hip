@@ -12,10 +12,13 @@
 // Built with the MFMA results in ordinary VGPRs (-amdgpu-mfma-vgpr-form): the
 // accumulator-register form costs one copy per result element here.
 //
-// Work: a workgroup is one wave, which takes 128 positions of one row as eight
-// 16-token tiles (longer waves, double-buffered or not, measured slower: what
-// pays is many waves with their loads in flight; workgroups of one wave beat
-// four, 37.2 -> 36.3 us cold on the 16 x 131072 decode, and eight, 38.5 us). Per tile and group of
+// Work: a workgroup is one wave, which takes 192 positions of one row as twelve
+// 16-token tiles. Measured cold on the 16 x 131072 decode: workgroups of one
+// wave beat four (37.2 -> 36.3 us at 8 tiles) and eight (38.5 us); with one
+// wave, 12 tiles (128 VGPRs, 4 waves per SIMD) 35.3 us, 16 tiles 35.3, 8 tiles
+// 36.0, 4 tiles 41.3, 24 tiles 37.5 and 32 tiles 39.7 (2 waves per SIMD); the
+// two-rows-per-sequence batch is fastest at 12 (19.6 us against 19.9 at 16).
+// Double-buffered waves measured slower. Per tile and group of
 // 16 heads, one
 // v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 on both sides gives
 // S[head][token]: A = the row's q (16 heads, loaded once per wave), B = the
@@ -48,7 +51,7 @@ typedef uint32_t mq_u32x4 __attribute__((ext_vector_type(4)));
 
 #define MQ_DEV __device__ __forceinline__
 
-constexpr int kMqTiles = 8;              // 16-token tiles per wave
+constexpr int kMqTiles = 12;             // 16-token tiles per wave
 constexpr int kMqWave = 16 * kMqTiles;   // positions per wave
 constexpr int kMqWaves = 1;              // waves per workgroup
 constexpr int kMqChunk = kMqWaves * kMqWave;  // positions per workgroup
@@ -142,9 +145,12 @@ __global__ __launch_bounds__(64 * kMqWaves) void pa_mqa_logits_mxfp4_kernel(cons
     // every lane group ends a tile with the same sum (the two lane swaps add
     // the same pairs, in either order), so lane (n, g) keeps the score of token
     // n of tile 4 h + g in keep[h]: lane l then holds position ws + 64 h + l,
-    // and each half of the wave's scores leaves in one store of 256 bytes
-    static_assert(kMqTiles == 8, "two stores of 64 positions");
-    float keep[2] = {0.f, 0.f};
+    // and each 64 positions of the wave's scores leave in one store of 256 bytes
+    static_assert(kMqTiles % 4 == 0, "whole stores of 64 positions");
+    constexpr int KH = kMqTiles / 4;
+    float keep[KH];
+#pragma unroll
+    for (int h = 0; h < KH; ++h) keep[h] = 0.f;
 
 #pragma unroll
     for (int j = 0; j < kMqTiles; ++j) {
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void pa_mqa_logits_mxfp4_kernel(cons
         if ((j & 3) == g) keep[j >> 2] = acc;
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < KH; ++h) {
         const int t = ws + 64 * h + lane;
         if (t >= t0 && t < t1) __builtin_nontemporal_store(keep[h], orow + t);  // written once, read later
     }
